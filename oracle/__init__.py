@@ -1,0 +1,216 @@
+"""fp64 CPU oracle for grouped-query attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg may
+import this package. It shares no code with the HIP path: the C source
+``gqa_oracle.c`` (built with gcc into ``liboracle.so``) computes attention from its
+definition in double precision, and ``brute.py`` repeats it in pure Python for tiny
+inputs. Inputs come from ``workloads.py``; bf16 and fp32 values convert exactly to
+float64, fp8 codes are decoded by the C oracle's own E4M3FN decoder.
+
+Which passage each function follows is stated in ``gqa_oracle.c``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "gqa_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_lp = ctypes.POINTER(ctypes.c_int64)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_fp = ctypes.POINTER(ctypes.c_float)
+
+
+def compile_c(src: str, out: str) -> str:
+    """gcc -O2 -fopenmp (no fast-math) of one oracle source into a shared library."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    """Compile liboracle.so from gqa_oracle.c."""
+    return compile_c(SOURCE, LIBRARY)
+
+
+def _f64(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu()
+        if x.dtype == torch.float8_e4m3fn:
+            raise TypeError("fp8 tensors need their scales: use dequant_e4m3fn")
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+class Oracle:
+    """ctypes view of one build of the C oracle."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.gqa_oracle_decode.argtypes = [_dp, _dp, _dp, _ip, _dp] + [ctypes.c_int] * 5 + [ctypes.c_double]
+        lib.gqa_oracle_decode.restype = ctypes.c_int
+        lib.gqa_oracle_decode_rows.argtypes = ([_dp, _dp, _dp, _ip] + [ctypes.c_int] * 5 +
+                                               [ctypes.c_double, _lp, ctypes.c_long, _dp])
+        lib.gqa_oracle_decode_rows.restype = ctypes.c_int
+        lib.gqa_oracle_prefill.argtypes = ([_dp, _dp, _dp, _dp] + [ctypes.c_int] * 5 +
+                                           [ctypes.c_double, ctypes.c_int])
+        lib.gqa_oracle_prefill.restype = ctypes.c_int
+        lib.gqa_oracle_prefill_rows.argtypes = ([_dp, _dp, _dp] + [ctypes.c_int] * 5 +
+                                                [ctypes.c_double, ctypes.c_int, _lp, ctypes.c_long, _dp])
+        lib.gqa_oracle_prefill_rows.restype = ctypes.c_int
+        lib.gqa_oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
+        lib.gqa_oracle_e4m3fn_value.restype = ctypes.c_double
+        lib.gqa_oracle_dequant_e4m3fn.argtypes = [_u8p, _fp, ctypes.c_long, ctypes.c_long, _dp]
+        lib.gqa_oracle_dequant_e4m3fn.restype = None
+        lib.gqa_oracle_num_threads.restype = ctypes.c_int
+        lib.gqa_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        self.lib = lib
+        self.path = path
+
+    # ---- threads -------------------------------------------------------------------
+    def num_threads(self) -> int:
+        return int(self.lib.gqa_oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.gqa_oracle_set_num_threads(int(n))
+
+    # ---- fp8 -----------------------------------------------------------------------
+    def e4m3fn_value(self, code: int) -> float:
+        return float(self.lib.gqa_oracle_e4m3fn_value(int(code) & 0xFF))
+
+    def dequant_e4m3fn(self, codes: torch.Tensor, scales: torch.Tensor) -> np.ndarray:
+        """codes [S, ...] float8_e4m3fn (or uint8), scales [S] float32 -> float64 code*scale."""
+        c = codes.detach().cpu().contiguous()
+        if c.dtype == torch.float8_e4m3fn:
+            c = c.view(torch.uint8)
+        cn = np.ascontiguousarray(c.numpy(), dtype=np.uint8)
+        sn = np.ascontiguousarray(scales.detach().cpu().to(torch.float32).numpy(), dtype=np.float32)
+        nslab = sn.shape[0]
+        slab_len = cn.size // nslab
+        assert nslab * slab_len == cn.size
+        out = np.empty(cn.shape, dtype=np.float64)
+        self.lib.gqa_oracle_dequant_e4m3fn(_ptr(cn, _u8p), _ptr(sn, _fp), nslab, slab_len, _ptr(out, _dp))
+        return out
+
+    # ---- decode --------------------------------------------------------------------
+    def decode_kv_f64(self, case):
+        """The K and V cache values a decode case stands for, as float64 arrays."""
+        if case.kv_dtype == "fp8_e4m3fn":
+            return (self.dequant_e4m3fn(case.k_cache, case.k_scale),
+                    self.dequant_e4m3fn(case.v_cache, case.v_scale))
+        return _f64(case.k_cache), _f64(case.v_cache)
+
+    def decode_arrays(self, q, k_cache, v_cache, seq_lens, scale) -> np.ndarray:
+        q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
+        B, H, D = q.shape
+        _, G, T_cap, _ = k.shape
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        out = np.empty((B, H, D), dtype=np.float64)
+        rc = self.lib.gqa_oracle_decode(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(sl, _ip),
+                                        _ptr(out, _dp), B, H, G, D, T_cap, float(scale))
+        if rc != 0:
+            raise ValueError(f"oracle decode rejected its arguments (code {rc})")
+        return out
+
+    def decode(self, case) -> np.ndarray:
+        """Oracle output [B, H, D] (float64) for a workloads.DecodeCase."""
+        k, v = self.decode_kv_f64(case)
+        return self.decode_arrays(case.q, k, v, case.seq_lens.numpy(), case.scale)
+
+    def decode_rows(self, case, rows, kv=None) -> np.ndarray:
+        """Oracle output for selected rows (b*H + h) -> [len(rows), D]."""
+        k, v = kv if kv is not None else self.decode_kv_f64(case)
+        q = _f64(case.q)
+        B, H, D = q.shape
+        _, G, T_cap, _ = k.shape
+        sl = np.ascontiguousarray(case.seq_lens.numpy().astype(np.int32))
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rc = self.lib.gqa_oracle_decode_rows(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(sl, _ip),
+                                             B, H, G, D, T_cap, float(case.scale), _ptr(r, _lp),
+                                             r.shape[0], _ptr(out, _dp))
+        if rc != 0:
+            raise ValueError(f"oracle decode_rows rejected its arguments (code {rc})")
+        return out
+
+    # ---- prefill -------------------------------------------------------------------
+    def prefill_arrays(self, q, k, v, scale, causal) -> np.ndarray:
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, T, D = q.shape
+        G = k.shape[1]
+        out = np.empty((B, H, T, D), dtype=np.float64)
+        rc = self.lib.gqa_oracle_prefill(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(out, _dp),
+                                         B, T, H, G, D, float(scale), int(bool(causal)))
+        if rc != 0:
+            raise ValueError(f"oracle prefill rejected its arguments (code {rc})")
+        return out
+
+    def prefill(self, case) -> np.ndarray:
+        """Oracle output [B, H, T, D] (float64) for a workloads.PrefillCase."""
+        return self.prefill_arrays(case.q, case.k, case.v, case.scale, case.causal)
+
+    def prefill_rows(self, case, rows, f64=None) -> np.ndarray:
+        """Oracle output for selected rows ((b*H + h)*T + i) -> [len(rows), D]."""
+        q, k, v = f64 if f64 is not None else (_f64(case.q), _f64(case.k), _f64(case.v))
+        B, H, T, D = q.shape
+        G = k.shape[1]
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rc = self.lib.gqa_oracle_prefill_rows(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), B, T, H, G, D,
+                                              float(case.scale), int(bool(case.causal)), _ptr(r, _lp),
+                                              r.shape[0], _ptr(out, _dp))
+        if rc != 0:
+            raise ValueError(f"oracle prefill_rows rejected its arguments (code {rc})")
+        return out
+
+
+_default = None
+
+
+def load() -> Oracle:
+    """The oracle built from gqa_oracle.c (compiled here if missing or stale)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def from_library(path: str) -> Oracle:
+    return Oracle(path)
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact float64 copy of an fp32/bf16 tensor or array."""
+    return _f64(x)
+
+
+# Module-level shortcuts onto the default build.
+def decode(case): return load().decode(case)
+def decode_rows(case, rows, kv=None): return load().decode_rows(case, rows, kv)
+def decode_arrays(*a): return load().decode_arrays(*a)
+def decode_kv_f64(case): return load().decode_kv_f64(case)
+def prefill(case): return load().prefill(case)
+def prefill_rows(case, rows, f64=None): return load().prefill_rows(case, rows, f64)
+def prefill_arrays(*a): return load().prefill_arrays(*a)
+def dequant_e4m3fn(codes, scales): return load().dequant_e4m3fn(codes, scales)
+def e4m3fn_value(code): return load().e4m3fn_value(code)
+def num_threads(): return load().num_threads()
+def set_num_threads(n): return load().set_num_threads(n)

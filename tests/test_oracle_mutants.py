@@ -1,0 +1,42 @@
+"""Planted mistakes in the oracle (CPU only): each mutated build of gqa_oracle.c
+must fail at least one pin, which shows the pins can see that kind of mistake."""
+
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, original text, mutated text): plausible slips in each part of the definition.
+MUTANTS = [
+    ("dropped_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("softmax_sign", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    ("tiled_head_map", "return h / (H / G);", "return h % G;"),
+    ("causal_excludes_diagonal", "long n = causal ? (long)i + 1 : (long)T;", "long n = causal ? (long)i : (long)T;"),
+    ("decode_drops_current_token", "long L = seq_lens[b];", "long L = seq_lens[b] - 1;"),
+    ("transposed_k", "dot += q[d] * K[j * (long)D + d];", "dot += q[d] * K[d * n + j];"),
+    ("transposed_v", "acc += s[j] * V[j * (long)D + d];", "acc += s[j] * V[d * n + j];"),
+    ("unnormalised_by_count", "out[d] = acc / denom;", "out[d] = acc / (double)n;"),
+    ("batch_group_swap", "((long)b * G + g) * T_cap * D", "((long)g * B + b) * T_cap * D"),
+    ("fp8_bias", "e - 7);", "e - 8);"),
+    ("fp8_subnormal", "(double)m / 8.0, -6);", "(double)m / 8.0, -7);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, orig, mut):
+    src = open(oracle.SOURCE).read()
+    assert orig in src, f"mutation site for {name} not found"
+    mutated = src.replace(orig, mut)
+    path = tmp_path / f"{name}.c"
+    path.write_text(mutated)
+    lib = oracle.compile_c(str(path), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.from_library(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,249 @@
+"""Seeded synthetic inputs for grouped-query attention (host tensors only).
+
+This module is shared by the tests, the benchmark and the oracle checks. It draws
+random numbers and lays them out in the storage formats the kernels read; it holds
+none of the attention arithmetic.
+
+Recipe (every workload):
+  * generator: ``torch.Generator('cpu').manual_seed(seed)``;
+  * draw order: per-sequence cache lengths (ragged decode only), then Q, then K,
+    then V, each ``torch.randn`` in float32 over the full allocated shape, then cast
+    to the storage dtype (bf16 rounding is round-to-nearest-even);
+  * KV-cache rows at or beyond a sequence's valid length are poisoned with NaN, so a
+    kernel that reads them produces NaN in its output;
+  * fp8 KV (OCP E4M3FN, largest finite value 448): one float32 scale per
+    (sequence, KV head) for K and one for V, each the absolute maximum of that
+    slab's valid rows divided by 448; codes are ``round_to_nearest_even(x / scale)``
+    via torch's cast. The stored value a code stands for is ``fp8(code) * scale``.
+
+Layouts (head-major, head dim innermost: the projections of the page "Hands-on:
+implementing GQA in PyTorch", section 1.1, are reshaped to batch, heads, sequence,
+head dim in that order):
+  decode  q / out    [B, H, D]
+          k / v cache [B, G, T_cap, D], seq_lens int32 [B]
+  prefill q / out    [B, H, T, D]
+          k / v      [B, G, T, D]
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+FP8 = "fp8_e4m3fn"
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn}
+FP8_MAX = 448.0
+
+
+@dataclass
+class DecodeCase:
+    """One single-token decode step over a KV cache."""
+
+    name: str
+    q: torch.Tensor            # [B, H, D] q_dtype
+    k_cache: torch.Tensor      # [B, G, T_cap, D] kv_dtype
+    v_cache: torch.Tensor      # [B, G, T_cap, D] kv_dtype
+    seq_lens: torch.Tensor     # [B] int32, valid rows per sequence (current token included)
+    scale: float
+    q_dtype: str
+    kv_dtype: str
+    k_scale: Optional[torch.Tensor] = None   # [B*G] float32, fp8 only
+    v_scale: Optional[torch.Tensor] = None   # [B*G] float32, fp8 only
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def D(self): return self.q.shape[2]
+    @property
+    def G(self): return self.k_cache.shape[1]
+    @property
+    def T_cap(self): return self.k_cache.shape[2]
+
+
+@dataclass
+class PrefillCase:
+    """Full-sequence (prefill) attention, causal or not."""
+
+    name: str
+    q: torch.Tensor   # [B, H, T, D]
+    k: torch.Tensor   # [B, G, T, D]
+    v: torch.Tensor   # [B, G, T, D]
+    scale: float
+    causal: bool
+    dtype: str
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def T(self): return self.q.shape[2]
+    @property
+    def D(self): return self.q.shape[3]
+    @property
+    def G(self): return self.k.shape[1]
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator("cpu").manual_seed(seed)
+
+
+def _randn(shape, g):
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def quantize_fp8_slabs(x: torch.Tensor, seq_lens: torch.Tensor):
+    """Store float32 ``x`` [B, G, T_cap, D] as E4M3FN codes with one scale per (b, g).
+
+    The scale is the slab's absolute maximum over its valid rows divided by 448; the
+    codes of padding rows are NaN. Returns (codes as float8_e4m3fn tensor, scales
+    float32 [B*G]).
+    """
+    B, G, T_cap, D = x.shape
+    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn)
+    scales = torch.empty(B * G, dtype=torch.float32)
+    for b in range(B):
+        L = int(min(max(int(seq_lens[b]), 0), T_cap))
+        for g in range(G):
+            slab = x[b, g, :L]
+            amax = float(slab.abs().max()) if L > 0 else 0.0
+            s = amax / FP8_MAX if amax > 0 else 1.0
+            s = float(torch.tensor(s, dtype=torch.float32))
+            scales[b * G + g] = s
+            q = torch.full((T_cap, D), float("nan"), dtype=torch.float32)
+            q[:L] = slab / s
+            codes[b, g] = q.to(torch.float8_e4m3fn)
+    return codes, scales
+
+
+def make_decode(B, H, G, D, seq_lens, T_cap=None, q_dtype=BF16, kv_dtype=BF16, seed=0,
+                name="decode", scale=None, poison=True) -> DecodeCase:
+    """Decode inputs. ``seq_lens`` is an int (same length for every sequence), a
+    list, or the string ``"uniform:lo:hi"`` for lengths drawn uniformly from
+    [lo, hi] inclusive (drawn first, before Q, K and V)."""
+    g = _gen(seed)
+    if isinstance(seq_lens, str) and seq_lens.startswith("uniform:"):
+        _, lo, hi = seq_lens.split(":")
+        lens = torch.randint(int(lo), int(hi) + 1, (B,), generator=g).to(torch.int32)
+    elif isinstance(seq_lens, int):
+        lens = torch.full((B,), seq_lens, dtype=torch.int32)
+    else:
+        lens = torch.tensor(list(seq_lens), dtype=torch.int32)
+        assert lens.numel() == B
+    if T_cap is None:
+        T_cap = max(int(lens.max()), 1)
+    q = _randn((B, H, D), g)
+    k = _randn((B, G, T_cap, D), g)
+    v = _randn((B, G, T_cap, D), g)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    k_scale = v_scale = None
+    if kv_dtype == FP8:
+        k_st, k_scale = quantize_fp8_slabs(k, lens)
+        v_st, v_scale = quantize_fp8_slabs(v, lens)
+    else:
+        if poison:
+            for b in range(B):
+                L = int(min(max(int(lens[b]), 0), T_cap))
+                k[b, :, L:] = float("nan")
+                v[b, :, L:] = float("nan")
+        k_st = k.to(_TORCH_DTYPE[kv_dtype])
+        v_st = v.to(_TORCH_DTYPE[kv_dtype])
+    return DecodeCase(name=name, q=q.to(_TORCH_DTYPE[q_dtype]), k_cache=k_st, v_cache=v_st,
+                      seq_lens=lens, scale=float(scale), q_dtype=q_dtype, kv_dtype=kv_dtype,
+                      k_scale=k_scale, v_scale=v_scale)
+
+
+def make_prefill(B, H, G, D, T, dtype=BF16, causal=True, seed=0, name="prefill",
+                 scale=None) -> PrefillCase:
+    g = _gen(seed)
+    q = _randn((B, H, T, D), g)
+    k = _randn((B, G, T, D), g)
+    v = _randn((B, G, T, D), g)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    td = _TORCH_DTYPE[dtype]
+    return PrefillCase(name=name, q=q.to(td), k=k.to(td), v=v.to(td), scale=float(scale),
+                       causal=causal, dtype=dtype)
+
+
+# --------------------------------------------------------------------------------------
+# The five named workloads.
+# --------------------------------------------------------------------------------------
+
+TOY_PREFILL_T = 5
+TOY_DECODE_LENS = (6, 7)
+
+
+def toy_tokens(seed=0):
+    """The 12-dim, 4-head toy of the tutorial pages: H=4, G=2, head dim 3, batch 1.
+
+    Seven tokens are drawn at once (q [1,4,7,3], k/v [1,2,7,3], fp32): the prefill
+    uses the first five, the two decode steps then append tokens 6 and 7.
+    """
+    g = _gen(seed)
+    q = _randn((1, 4, 7, 3), g)
+    k = _randn((1, 2, 7, 3), g)
+    v = _randn((1, 2, 7, 3), g)
+    return q, k, v
+
+
+def toy_prefill(seed=0) -> PrefillCase:
+    q, k, v = toy_tokens(seed)
+    T = TOY_PREFILL_T
+    return PrefillCase(name="toy_prefill", q=q[:, :, :T].contiguous(), k=k[:, :, :T].contiguous(),
+                       v=v[:, :, :T].contiguous(), scale=1.0 / math.sqrt(3.0), causal=True, dtype=F32)
+
+
+def toy_decode_steps(seed=0, T_cap=8):
+    """The two decode steps after the toy prefill: cache lengths 6 and 7."""
+    q, k, v = toy_tokens(seed)
+    steps = []
+    for L in TOY_DECODE_LENS:
+        kc = torch.full((1, 2, T_cap, 3), float("nan"))
+        vc = torch.full((1, 2, T_cap, 3), float("nan"))
+        kc[:, :, :L] = k[:, :, :L]
+        vc[:, :, :L] = v[:, :, :L]
+        steps.append(DecodeCase(name=f"toy_decode_L{L}", q=q[:, :, L - 1].contiguous(), k_cache=kc,
+                                v_cache=vc, seq_lens=torch.tensor([L], dtype=torch.int32),
+                                scale=1.0 / math.sqrt(3.0), q_dtype=F32, kv_dtype=F32))
+    return steps
+
+
+def llama7b_gqa8_decode(seed=0) -> DecodeCase:
+    """Llama-2-7B-shaped GQA-8 decode: B1 H32 G8 D128, cache of 2048 tokens, bf16."""
+    return make_decode(1, 32, 8, 128, 2048, T_cap=2048, seed=seed, name="llama7b_gqa8_decode_L2048")
+
+
+def llama70b_ragged_decode(seed=0) -> DecodeCase:
+    """Llama-2-70B-shaped decode: B16 H64 G8 D128, lengths ~ U[1024, 4096], T_cap 4096."""
+    return make_decode(16, 64, 8, 128, "uniform:1024:4096", T_cap=4096, seed=seed,
+                       name="llama70b_gqa8_decode_B16_ragged")
+
+
+def causal_prefill_2048(seed=0) -> PrefillCase:
+    """Causal GQA prefill: B4 H32 G8 D128 T2048, bf16."""
+    return make_prefill(4, 32, 8, 128, 2048, seed=seed, name="gqa8_causal_prefill_B4_T2048")
+
+
+def mqa_fp8_long_decode(seed=0) -> DecodeCase:
+    """Long-context MQA decode: B8 H32 G1 D128, 32768 cached tokens, fp8-E4M3FN KV."""
+    return make_decode(8, 32, 1, 128, 32768, T_cap=32768, kv_dtype=FP8, seed=seed,
+                       name="mqa_fp8_decode_B8_L32768")
+
+
+WORKLOADS = {
+    "toy": None,  # prefill + two decode steps; see toy_prefill / toy_decode_steps
+    "llama7b_gqa8_decode_L2048": llama7b_gqa8_decode,
+    "llama70b_gqa8_decode_B16_ragged": llama70b_ragged_decode,
+    "gqa8_causal_prefill_B4_T2048": causal_prefill_2048,
+    "mqa_fp8_decode_B8_L32768": mqa_fp8_long_decode,
+}
