@@ -1,0 +1,282 @@
+"""Benchmark of the GQA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-breakdown]
+
+A step is one call of the hot path over one batch of synthetic inputs (seeded, from
+workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H32 G8
+D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
+B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown".
+
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronisations. Each step reads the next of several replicas of its inputs, together
+at least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set and the
+figures are HBM figures. HIP events recorded on the launch stream around every call
+give the per-launch duration used for the roofline.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+COLD_BYTES = 1 << 30            # replicas rotate through at least this much memory
+
+HEADLINE = "llama7b_gqa8_decode_L2048"
+METRIC = "GQA decode KV-read GB/s (% HBM peak) + tok/s; prefill TFLOP/s (% MFMA peak)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------
+# Algorithmic work per call (what the method must move / compute, nothing more).
+# ------------------------------------------------------------------------------------
+
+def decode_bytes(c: W.DecodeCase) -> dict:
+    """KV bytes = valid rows only: 2 (K and V) x sum_b L_b x G x D x element size."""
+    esz = {W.F32: 4, W.BF16: 2, W.FP8: 1}
+    lens = c.seq_lens.clamp(0, c.T_cap).to(torch.int64)
+    kv = 2 * int(lens.sum()) * c.G * c.D * esz[c.kv_dtype]
+    qo = 2 * c.B * c.H * c.D * esz[c.q_dtype]
+    extra = 4 * c.B + (8 * c.B * c.G if c.kv_dtype == W.FP8 else 0)   # seq_lens (+ fp8 scales)
+    return {"kv": kv, "total": kv + qo + extra}
+
+
+def decode_flops(c: W.DecodeCase) -> int:
+    lens = c.seq_lens.clamp(0, c.T_cap).to(torch.int64)
+    return 4 * c.H * c.D * int(lens.sum())
+
+
+def prefill_flops(c: W.PrefillCase) -> int:
+    """Causal: position i attends to i + 1 keys (diagonal included); 4*D flops per pair."""
+    pairs = c.T * (c.T + 1) // 2 if c.causal else c.T * c.T
+    return 4 * c.B * c.H * c.D * pairs
+
+
+def prefill_bytes(c: W.PrefillCase) -> int:
+    esz = 4 if c.dtype == W.F32 else 2
+    return esz * (2 * c.q.numel() + c.k.numel() + c.v.numel())
+
+
+# ------------------------------------------------------------------------------------
+
+def make_decode_runner(gqa, c: W.DecodeCase, dev):
+    kv_alloc = 2 * c.k_cache.numel() * c.k_cache.element_size()
+    nrep = max(1, math.ceil(COLD_BYTES / kv_alloc))
+    reps = []
+    base = [c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)]
+    for i in range(nrep):
+        reps.append(base if i == 0 else [t.clone() for t in base])
+    lens = c.seq_lens.to(dev)
+    ks = c.k_scale.to(dev) if c.k_scale is not None else None
+    vs = c.v_scale.to(dev) if c.v_scale is not None else None
+    out = torch.empty_like(base[0])
+    ws_bytes = gqa.decode_workspace_size(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    state = {"i": 0}
+
+    def step():
+        q, k, v = reps[state["i"] % nrep]
+        state["i"] += 1
+        gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws)
+
+    return step, nrep, out
+
+
+def make_prefill_runner(gqa, c: W.PrefillCase, dev):
+    per = prefill_bytes(c)
+    nrep = max(1, math.ceil(COLD_BYTES / per))
+    base = [c.q.to(dev), c.k.to(dev), c.v.to(dev)]
+    reps = [base if i == 0 else [t.clone() for t in base] for i in range(nrep)]
+    out = torch.empty_like(base[0])
+    state = {"i": 0}
+
+    def step():
+        q, k, v = reps[state["i"] % nrep]
+        state["i"] += 1
+        gqa.prefill(q, k, v, out=out, scale=c.scale, causal=c.causal)
+
+    return step, nrep, out
+
+
+def time_steps(step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {"ms_per_step": total_ms / steps, "launch_ms_mean": sum(per) / len(per),
+            "launch_ms_median": per[len(per) // 2], "launch_ms_p10": per[len(per) // 10],
+            "launch_ms_p90": per[(9 * len(per)) // 10]}
+
+
+def bench_decode(gqa, c, steps, warmup, dev):
+    step, nrep, _ = make_decode_runner(gqa, c, dev)
+    t = time_steps(step, steps, warmup)
+    by = decode_bytes(c)
+    s = t["ms_per_step"] * 1e-3
+    launch = t["launch_ms_mean"] * 1e-3
+    achieved = by["total"] / launch / 1e9
+    return {
+        "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T_cap": c.T_cap,
+        "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype,
+        "splits": gqa.decode_num_splits(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype),
+        "kv_bytes": by["kv"], "algorithmic_bytes": by["total"], "flops": decode_flops(c),
+        "kv_read_GBps": by["kv"] / s / 1e9, "tok_per_s": c.B / s,
+        "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
+        "launch_us_median": t["launch_ms_median"] * 1e3, "launch_us_p10": t["launch_ms_p10"] * 1e3,
+        "launch_us_p90": t["launch_ms_p90"] * 1e3, "replicas": nrep,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+
+
+def bench_prefill(gqa, c, steps, warmup, dev):
+    step, nrep, _ = make_prefill_runner(gqa, c, dev)
+    t = time_steps(step, steps, warmup)
+    fl = prefill_flops(c)
+    s = t["ms_per_step"] * 1e-3
+    launch = t["launch_ms_mean"] * 1e-3
+    achieved = fl / launch / 1e12
+    return {
+        "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T": c.T, "causal": c.causal,
+        "flops": fl, "algorithmic_bytes": prefill_bytes(c), "tflops": fl / s / 1e12,
+        "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
+        "launch_us_median": t["launch_ms_median"] * 1e3, "replicas": nrep,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+    }
+
+
+def cpu_baseline_decode(c: W.DecodeCase, budget_s=10.0):
+    """The fp64 oracle on the host cores, on the same decode step (whole step, repeated)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(threads)
+    k, v = oracle.decode_kv_f64(c)
+    q = oracle.to_f64(c.q)
+    lens = c.seq_lens.numpy()
+    times = []
+    t_stop = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_arrays(q, k, v, lens, c.scale)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_stop or len(times) >= 2000:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    by = decode_bytes(c)
+    return {"value": by["kv"] / med / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"whole {c.name} decode step (fp64 C oracle, OpenMP), median of {len(times)} runs; "
+                      f"{med * 1e3:.2f} ms per step, {c.B / med:.1f} tok/s",
+            "seconds_per_step": med}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, choices=[k for k in W.WORKLOADS if k != "toy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import grouped_query_attention_decode_amd as gqa
+    gqa.library()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def run(name, steps, warmup):
+        case = W.WORKLOADS[name](0)
+        log(f"[bench] {name}: steps={steps} warmup={warmup}")
+        if isinstance(case, W.PrefillCase):
+            r = bench_prefill(gqa, case, steps, warmup, dev)
+        else:
+            r = bench_decode(gqa, case, steps, warmup, dev)
+        log(f"[bench] {name}: {json.dumps(r)}")
+        return case, r
+
+    case, head = run(args.workload, args.steps, args.warmup)
+    breakdown = {}
+    if not args.no_breakdown:
+        for name in W.WORKLOADS:
+            if name in ("toy", args.workload):
+                continue
+            _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
+            breakdown[name] = r
+
+    is_prefill = isinstance(case, W.PrefillCase)
+    cpu = None
+    if not args.no_cpu_baseline and not is_prefill:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline_decode(case)
+        log(f"[bench] cpu baseline: {json.dumps(cpu)}")
+
+    if is_prefill:
+        value, unit, dtype = head["tflops"], "TFLOP/s", "bf16"
+    else:
+        value, unit = head["kv_read_GBps"], "GB/s"
+        dtype = {W.BF16: "bf16", W.FP8: "fp8_e4m3fn", W.F32: "f32"}[case.kv_dtype]
+    cfg = {"workload": case.name, "global_batch": case.B, "heads": case.H, "kv_heads": case.G,
+           "head_dim": case.D, "parallelism": "none (1 GPU)"}
+    if is_prefill:
+        cfg["seq_len"] = case.T
+    else:
+        cfg["kv_cache_len"] = case.T_cap
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1))",
+        "config": cfg,
+        "tok_per_s": head.get("tok_per_s"),
+        "hbm_frac": (value / HBM_PEAK_GBS) if not is_prefill else None,
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "detail": head,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+"""Python binding of libgqa.so: grouped-query attention decode and prefill on MI355X.
+
+Argument marshalling only. Every step of the computation runs in the HIP kernels of
+libgqa.so, reached through its C ABI (include/gqa.h); torch supplies device memory and
+the current stream. There is no fallback: if the library is not built, or the device is
+not gfx950, calls raise.
+
+    decode(q, k_cache, v_cache, seq_lens, ...)   q [B,H,D], caches [B,G,T_cap,D]
+    prefill(q, k, v, causal=True, ...)           q [B,H,T,D], k/v [B,G,T,D]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
+
+__all__ = ["decode", "prefill", "decode_num_splits", "decode_workspace_size", "status_string",
+           "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES"]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+
+GQA_OK = 0
+DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3fn": 2}
+PATHS = {"auto": 0, "generic": 1, "valu": 2, "mfma": 3}
+_TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} ({status})")
+
+
+class GqaOpts(ctypes.Structure):
+    """Mirror of gqa_opts in include/gqa.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def library() -> ctypes.CDLL:
+    """Load libgqa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(f"{LIBRARY_PATH} is not built: run "
+                           "`python -m grouped_query_attention_decode_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.gqa_opts_init.argtypes = [ctypes.POINTER(GqaOpts)]
+    lib.gqa_opts_init.restype = None
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_decode.restype = i
+    lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_prefill.restype = i
+    lib.gqa_decode_num_splits.argtypes = [i] * 7
+    lib.gqa_decode_num_splits.restype = i
+    lib.gqa_decode_workspace_size.argtypes = [i] * 7
+    lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.gqa_status_string.argtypes = [i]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped ({sorted(runtimes)}); streams would not be shared")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().gqa_status_string(int(status)).decode()
+
+
+def new_opts(**fields) -> GqaOpts:
+    o = GqaOpts()
+    library().gqa_opts_init(ctypes.byref(o))
+    for k, v in fields.items():
+        setattr(o, k, v)
+    return o
+
+
+def _kv_code(kv_dtype) -> int:
+    return kv_dtype if isinstance(kv_dtype, int) else DTYPES[kv_dtype]
+
+
+def decode_num_splits(B, H, G, D, kv_capacity, kv_dtype="bf16", num_splits=0) -> int:
+    """KV splits gqa_decode uses for these sizes (0 for invalid sizes)."""
+    return int(library().gqa_decode_num_splits(B, H, G, D, kv_capacity, _kv_code(kv_dtype), num_splits))
+
+
+def decode_workspace_size(B, H, G, D, kv_capacity, kv_dtype="bf16", num_splits=0) -> int:
+    """Device workspace bytes gqa_decode needs for these sizes (0: none)."""
+    return int(library().gqa_decode_workspace_size(B, H, G, D, kv_capacity, _kv_code(kv_dtype), num_splits))
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype not in _TORCH_TO_CODE:
+        raise TypeError(f"{what}: unsupported dtype {t.dtype}")
+    return _TORCH_TO_CODE[t.dtype]
+
+
+def _need_cuda(t: torch.Tensor, what: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
+           num_splits=0, path="auto", workspace=None, stream=None):
+    """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [B,H,D] and k_cache, v_cache [B,G,T_cap,D]")
+    B, H, D = q.shape
+    Bk, G, T_cap, Dk = k_cache.shape
+    if Bk != B or Dk != D or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens (int32 [B])")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kv_code = _dtype_code(k_cache, "k_cache")
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
+                 num_splits=int(num_splits), path=PATHS[path])
+    if kv_code == DTYPES["fp8_e4m3fn"]:
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 caches need k_scale and v_scale")
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need_cuda(t, n)
+            if t.dtype != torch.float32 or t.numel() != B * G:
+                raise ValueError(f"{n} must be float32 [B*G]")
+        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    need = decode_workspace_size(B, H, G, D, T_cap, kv_code, int(num_splits))
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        o.workspace, o.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = library().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                              out.data_ptr(), B, H, G, D, float(scale), _stream_handle(stream, q.device),
+                              ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_decode")
+    return out
+
+
+def prefill(q, k, v, out=None, scale=None, causal=True, path="auto", stream=None):
+    """GQA prefill (causal by default). Returns ``out`` [B, H, T, D] (q's dtype)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need_cuda(t, n)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,H,T,D] and k, v [B,G,T,D]")
+    B, H, T, D = q.shape
+    Bk, G, Tk, Dk = k.shape
+    if (Bk, Tk, Dk) != (B, T, D):
+        raise ValueError("shape mismatch between q and k/v")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=_dtype_code(k, "k"), path=PATHS[path])
+    st = library().gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, T, H, G, D,
+                               float(scale), int(bool(causal)), _stream_handle(stream, q.device),
+                               ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_prefill")
+    return out

@@ -1,0 +1,46 @@
+// Device-side element conversions used by the kernels of libgqa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// bf16 is the upper half of an IEEE binary32: widening is a shift.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3FN -> binary32, exact. Layout s.eeee.mmm, exponent bias 7; exponent field 0
+// holds subnormals m * 2^-9; s.1111.111 is NaN; there are no infinities.
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t e = (c >> 3) & 0xFu;
+    const uint32_t m = c & 0x7u;
+    if (e == 0xFu && m == 0x7u) return __uint_as_float(0x7fc00000u | sign);
+    if (e == 0u) {
+        const float mag = (float)m * 0.001953125f;  // m * 2^-9
+        return sign ? -mag : mag;
+    }
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));  // rebias 7 -> 127
+}
+
+template <int KVT> struct KvElem;
+template <> struct KvElem<0> { using T = float; };
+template <> struct KvElem<1> { using T = uint16_t; };
+template <> struct KvElem<2> { using T = uint8_t; };
+
+__device__ __forceinline__ float load_f32(const float *p, long i) { return p[i]; }
+__device__ __forceinline__ float load_f32(const uint16_t *p, long i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float load_f32(const uint8_t *p, long i) { return e4m3fn_to_f32(p[i]); }
+
+__device__ __forceinline__ void store_f32(float *p, long i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_f32(uint16_t *p, long i, float x) { p[i] = f32_to_bf16(x); }
+
+}  // namespace gqa

@@ -1,0 +1,248 @@
+// Host layer of libgqa.so: the C ABI declared in include/gqa.h.
+//
+// Every check runs before the first HIP call, so a rejected call leaves the device and
+// the stream untouched. The launch sequence is: (optional) stream-ordered workspace,
+// the attention kernel, the split-KV combine when the cache was split, and the release
+// of the workspace -- all on the caller's stream, with no host synchronisation.
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "gqa.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kMaxDim = 256;
+constexpr int kMaxSplitsAbi = 1024;
+constexpr int kNumDevicesMax = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1; }
+
+bool valid_dtype(int dt) { return dt == DT_F32 || dt == DT_BF16 || dt == DT_FP8; }
+
+// Copy the caller's options over defaults, honouring struct_size (older, shorter
+// layouts keep the defaults for the fields they do not have).
+bool read_opts(const gqa_opts *in, gqa_opts *o) {
+    gqa_opts_init(o);
+    if (!in) return true;
+    if (in->struct_size < offsetof(gqa_opts, kv_dtype) + sizeof(int32_t)) return false;
+    const size_t n = in->struct_size < sizeof(gqa_opts) ? in->struct_size : sizeof(gqa_opts);
+    memcpy(o, in, n);
+    o->struct_size = sizeof(gqa_opts);
+    return true;
+}
+
+// Key-range splits for decode. A split is the unit of work of one workgroup. Aim at
+// about two workgroups per compute unit on the 256-CU part, but keep each split long
+// enough that its partial results (R heads x (D + 2) floats, written and read once) stay
+// under 1/8 of the K/V bytes it streams, and at least one 64-key tile long.
+int auto_splits(long B, long H, long G, long D, long T_cap, int kv_dtype) {
+    const long R = H / G;
+    const long units = B * G;
+    const long target = 512;
+    long min_len = (8L * R * (D + 2) * 4 * 2) / (2L * D * elem_bytes(kv_dtype));
+    if (min_len < 64) min_len = 64;
+    long by_len = (T_cap + min_len - 1) / min_len;
+    long by_units = (target + units - 1) / units;
+    long s = by_len < by_units ? by_len : by_units;
+    if (s < 1) s = 1;
+    if (s > kMaxSplitsAbi) s = kMaxSplitsAbi;
+    return (int)s;
+}
+
+bool decode_sizes_ok(int B, int H, int G, int D, int T_cap) {
+    if (B < 1 || H < 1 || G < 1 || D < 1 || T_cap < 1) return false;
+    if (H % G != 0 || D > kMaxDim) return false;
+    // Element counts must stay well inside int64 and grid sizes inside 2^31.
+    const double kv = (double)B * G * (double)T_cap * D;
+    if (kv > 9.0e15) return false;
+    if ((double)B * H > 2.0e9 || (double)B * G * H > 2.0e9) return false;
+    return true;
+}
+
+int resolve_splits(int B, int H, int G, int D, int T_cap, int kv_dtype, int requested) {
+    int s = requested > 0 ? requested : auto_splits(B, H, G, D, T_cap, kv_dtype);
+    if (s > T_cap) s = requested > 0 ? s : T_cap;
+    return s;
+}
+
+size_t workspace_bytes_for(long B, long H, long D, long S) {
+    if (S <= 1) return 0;
+    const size_t acc = (size_t)B * H * S * D * sizeof(float);
+    const size_t ml = (size_t)B * H * S * 2 * sizeof(float);
+    const size_t align = 256;
+    return ((acc + align - 1) / align) * align + ml;
+}
+
+// gfx950 check, once per device.
+std::mutex g_arch_mu;
+signed char g_arch_ok[kNumDevicesMax];  // 0 unknown, 1 ok, -1 not gfx950
+
+gqa_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GQA_ERR_HIP;
+    if (dev < 0 || dev >= kNumDevicesMax) return GQA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_arch_mu);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GQA_ERR_HIP;
+        g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_arch_ok[dev] == 1 ? GQA_OK : GQA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace gqa
+
+using namespace gqa;
+
+extern "C" {
+
+void gqa_opts_init(gqa_opts *o) {
+    if (!o) return;
+    memset(o, 0, sizeof(*o));
+    o->struct_size = sizeof(gqa_opts);
+    o->q_dtype = GQA_DTYPE_BF16;
+    o->kv_dtype = GQA_DTYPE_BF16;
+    o->path = GQA_PATH_AUTO;
+}
+
+const char *gqa_status_string(gqa_status s) {
+    switch (s) {
+        case GQA_OK: return "GQA_OK";
+        case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG";
+        case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+        case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+        case GQA_ERR_HIP: return "GQA_ERR_HIP";
+    }
+    return "GQA_ERR_UNKNOWN";
+}
+
+int gqa_decode_num_splits(int B, int H, int G, int D, int kv_capacity, int kv_dtype, int num_splits) {
+    if (!decode_sizes_ok(B, H, G, D, kv_capacity) || !valid_dtype(kv_dtype)) return 0;
+    if (num_splits < 0 || num_splits > kMaxSplitsAbi) return 0;
+    return resolve_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
+}
+
+size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, int kv_dtype, int num_splits) {
+    const int S = gqa_decode_num_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
+    if (S == 0) return SIZE_MAX;
+    return workspace_bytes_for(B, H, D, S);
+}
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                      void *out, int B, int H, int G, int D, float scale, hipStream_t stream,
+                      const gqa_opts *opts_in) {
+    // ---- host-side validation (no HIP calls) ----
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
+    gqa_opts o;
+    if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
+    if (o.reserved0 != 0) return GQA_ERR_INVALID_ARG;
+    if (!decode_sizes_ok(B, H, G, D, o.kv_capacity)) return GQA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+    if (o.num_splits < 0 || o.num_splits > kMaxSplitsAbi) return GQA_ERR_INVALID_ARG;
+    if (o.path < GQA_PATH_AUTO || o.path > GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
+    const bool pair_ok = (o.q_dtype == DT_F32 && o.kv_dtype == DT_F32) ||
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_BF16) ||
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8);
+    if (!pair_ok) return GQA_ERR_UNSUPPORTED;
+    if (o.kv_dtype == DT_FP8 && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.seq_lens = seq_lens;
+    a.k_scale = o.kv_dtype == DT_FP8 ? o.k_scale : nullptr;
+    a.v_scale = o.kv_dtype == DT_FP8 ? o.v_scale : nullptr;
+    a.B = B; a.H = H; a.G = G; a.D = D;
+    a.Tq = 1; a.Tk = o.kv_capacity;
+    a.causal = 0; a.decode = 1;
+    a.scale_log2 = scale * kLog2e;
+    a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
+    a.num_splits = resolve_splits(B, H, G, D, o.kv_capacity, o.kv_dtype, o.num_splits);
+    a.split_len = (o.kv_capacity + a.num_splits - 1) / a.num_splits;
+
+    int path = o.path;
+    if (path == GQA_PATH_AUTO) {
+        const int R = H / G;
+        if (decode_mfma_supports(a) && (R >= 8 || o.kv_dtype == DT_FP8)) path = GQA_PATH_MFMA;
+        else if (decode_valu_supports(a)) path = GQA_PATH_VALU;
+        else path = GQA_PATH_GENERIC;
+    }
+    if (path == GQA_PATH_VALU && !decode_valu_supports(a)) return GQA_ERR_UNSUPPORTED;
+    if (path == GQA_PATH_MFMA && !decode_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
+
+    const size_t need = workspace_bytes_for(B, H, D, a.num_splits);
+    if (need > 0 && o.workspace && o.workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    if (need > 0 && o.workspace && ((uintptr_t)o.workspace % 16) != 0) return GQA_ERR_INVALID_ARG;
+
+    // ---- device work ----
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+
+    void *ws = o.workspace;
+    bool owned = false;
+    if (need > 0 && !ws) {
+        if (hipMallocAsync(&ws, need, stream) != hipSuccess) return GQA_ERR_HIP;
+        owned = true;
+    }
+    if (need > 0) {
+        const size_t acc_bytes = (size_t)B * H * a.num_splits * D * sizeof(float);
+        a.part_acc = static_cast<float *>(ws);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((acc_bytes + 255) / 256) * 256);
+    }
+
+    hipError_t e;
+    if (path == GQA_PATH_MFMA) e = launch_decode_mfma(a, stream);
+    else if (path == GQA_PATH_VALU) e = launch_decode_valu(a, stream);
+    else e = launch_generic(a, stream);
+    if (e == hipSuccess && a.num_splits > 1) e = launch_combine(a, stream);
+    if (owned) {
+        const hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = f;
+    }
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, int B, int T, int H, int G,
+                       int D, float scale, int causal, hipStream_t stream, const gqa_opts *opts_in) {
+    if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+    gqa_opts o;
+    if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
+    if (o.reserved0 != 0) return GQA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || H < 1 || G < 1 || D < 1 || H % G != 0 || D > kMaxDim) return GQA_ERR_INVALID_ARG;
+    if ((double)B * H * (double)T * D > 9.0e15 || (double)B * G * H * (double)T > 2.0e9)
+        return GQA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+    if (o.path < GQA_PATH_AUTO || o.path > GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
+    if (o.q_dtype != o.kv_dtype || o.q_dtype == DT_FP8) return GQA_ERR_UNSUPPORTED;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.B = B; a.H = H; a.G = G; a.D = D;
+    a.Tq = T; a.Tk = T;
+    a.causal = causal; a.decode = 0;
+    a.num_splits = 1; a.split_len = T;
+    a.scale_log2 = scale * kLog2e;
+    a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
+
+    int path = o.path;
+    if (path == GQA_PATH_AUTO) path = prefill_mfma_supports(a) ? GQA_PATH_MFMA : GQA_PATH_GENERIC;
+    if (path == GQA_PATH_VALU) return GQA_ERR_UNSUPPORTED;
+    if (path == GQA_PATH_MFMA && !prefill_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
+
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+    const hipError_t e = path == GQA_PATH_MFMA ? launch_prefill_mfma(a, stream) : launch_generic(a, stream);
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal declarations shared by the host layer and the kernel sources of libgqa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// Everything one attention launch needs. Pointers are device pointers.
+struct AttnArgs {
+    const void *q;            // decode [B,H,D]; prefill [B,H,T,D]
+    const void *k;            // decode [B,G,T_cap,D]; prefill [B,G,T,D]
+    const void *v;
+    void *out;                // same shape and type as q
+    const int32_t *seq_lens;  // decode only
+    const float *k_scale;     // fp8 only, [B*G]
+    const float *v_scale;
+    float *part_acc;          // split partials, [B*H][S][D] (unnormalised)
+    float *part_ml;           // split partials, [B*H][S][2] = (running max, running sum)
+    int B, H, G, D;
+    int Tq;                   // query rows per (b, h): 1 for decode, T for prefill
+    int Tk;                   // key rows allocated per (b, g): T_cap or T
+    int causal;               // prefill: 1 = keys j <= i only
+    int decode;               // 1 = keys limited by seq_lens[b], query at row L-1
+    int num_splits;           // decode: number of key ranges (1 = write out directly)
+    int split_len;            // decode: keys per range
+    float scale_log2;         // scale * log2(e): scores are kept in the base-2 domain
+    int q_dtype, kv_dtype;
+};
+
+hipError_t launch_generic(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_decode_valu(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream);
+
+// Shape limits of the fast kernels (checked on the host before launch).
+bool decode_valu_supports(const AttnArgs &a);
+bool decode_mfma_supports(const AttnArgs &a);
+bool prefill_mfma_supports(const AttnArgs &a);
+
+}  // namespace gqa

@@ -1,0 +1,160 @@
+/*
+ * gqa.h -- C ABI of libgqa.so: grouped-query attention (GQA) decode and prefill on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Grouped-query attention splits H query heads into G groups of R = H / G
+ * consecutive heads; all heads of group g read the single key/value head g, so
+ * G = H is multi-head attention and G = 1 is multi-query attention [GQA paper
+ * digest page (51969.com), section "Grouped-query attention (GQA)", Figure 2;
+ * "LLM principles -- code implementation of multi-head attention (MQA and GQA)",
+ * section 5, where a head's group is its index divided by the heads per group].
+ * Query head h therefore reads KV head h / R. The library never copies a KV head
+ * out to its R query heads: every key/value row is read from memory once per
+ * (sequence, KV head) and used by all R heads of the group.
+ *
+ * For one query row q and key/value rows 0..n-1 the library computes
+ *     out = sum_j softmax_j(scale * q . k_j) * v_j
+ * ["LLM principles -- code ...", sections 3 and 5: Q times K transposed, divided by
+ * the square root of the head size, softmax over the keys, times V]. Callers
+ * normally pass scale = 1/sqrt(D).
+ *
+ * Memory: every pointer argument is caller-owned memory. Tensor pointers and
+ * seq_lens, k_scale, v_scale and workspace are DEVICE pointers; the options struct
+ * is a HOST pointer read during the call only. The library frees nothing it did
+ * not allocate, keeps no per-call state, and may be called from several host
+ * threads at once. Outputs must not alias inputs.
+ *
+ * Execution: both compute calls only enqueue work on `stream` and return without
+ * waiting; `out` is valid once the stream has drained. Results are deterministic
+ * for fixed arguments (no floating-point atomics).
+ *
+ * Errors: every call returns a gqa_status by value and never aborts or prints.
+ * All argument checks run on the host before any HIP call, so a rejected call has
+ * touched neither the device nor the stream. GQA_ERR_HIP reports a failure of the
+ * HIP runtime (for example a launch error) after work may have been enqueued.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, H % G != 0, non-finite scale, ... */
+    GQA_ERR_UNSUPPORTED = 2,   /* dtype pair, head dim, forced path or device not supported */
+    GQA_ERR_WORKSPACE = 3,     /* caller workspace smaller than gqa_decode_workspace_size() */
+    GQA_ERR_HIP = 4            /* the HIP runtime reported an error */
+} gqa_status;
+
+/* Element types. q and out always share one type. */
+typedef enum gqa_dtype {
+    GQA_DTYPE_F32 = 0,
+    GQA_DTYPE_BF16 = 1,
+    /* OCP 8-bit float E4M3FN (bias 7, no infinities, max 448). KV cache only; each
+     * stored value stands for code * scale with one fp32 scale per (sequence, KV
+     * head) ["GQA revolution: how xformers speeds up LLM inference", section on
+     * mixed-precision KV storage]. */
+    GQA_DTYPE_FP8_E4M3FN = 2
+} gqa_dtype;
+
+/* Kernel family for decode. AUTO picks by shape; the others force a family so tests
+ * can check each against the same inputs. */
+typedef enum gqa_path {
+    GQA_PATH_AUTO = 0,
+    GQA_PATH_GENERIC = 1,  /* any head dim 1..256, any supported dtype pair */
+    GQA_PATH_VALU = 2,     /* vector-ALU dot products; bf16 KV, D = 128 */
+    GQA_PATH_MFMA = 3      /* matrix cores; bf16 or fp8 KV, bf16 q, D = 128 */
+} gqa_path;
+
+typedef struct gqa_opts {
+    size_t struct_size;     /* sizeof(gqa_opts); fields past it are taken as defaults */
+    int32_t q_dtype;        /* gqa_dtype of q and out (default BF16) */
+    int32_t kv_dtype;       /* gqa_dtype of k/v or of the cache (default BF16) */
+    int32_t kv_capacity;    /* decode: T_cap, rows allocated per (sequence, KV head); required */
+    int32_t num_splits;     /* decode: KV splits per (sequence, KV head); 0 = choose */
+    int32_t path;           /* gqa_path (default AUTO) */
+    int32_t reserved0;      /* must be 0 */
+    const float *k_scale;   /* fp8 KV: device fp32 [B*G], index b*G + g; else NULL */
+    const float *v_scale;   /* fp8 KV: device fp32 [B*G]; else NULL */
+    void *workspace;        /* device scratch for split partials, or NULL */
+    size_t workspace_bytes; /* size of `workspace` */
+} gqa_opts;
+
+/* Fill `opts` with defaults: struct_size set, BF16/BF16, kv_capacity 0 (must be set
+ * for decode), num_splits 0, path AUTO, no scales, no workspace. */
+void gqa_opts_init(gqa_opts *opts);
+
+/*
+ * Single-token decode over a KV cache (the memory-bound step: the step reads the
+ * whole cache once [GQA paper digest page, section "QA": decoding is bound by
+ * loading the KV cache]).
+ *
+ *   q        [B, H, D]            q_dtype, the current token's query heads
+ *   k_cache  [B, G, T_cap, D]     kv_dtype, head dim innermost, T_cap = opts->kv_capacity
+ *   v_cache  [B, G, T_cap, D]     kv_dtype
+ *   seq_lens [B] int32 (device)   valid rows of sequence b, current token included
+ *   out      [B, H, D]            q_dtype
+ *
+ * The caller has already written the current token's k and v at row seq_lens[b]-1
+ * ("LLM principles -- code ...", sections 3 and 5 concatenate the new K/V to the
+ * cache before forming scores), so query head h of sequence b attends to rows
+ * 0 .. seq_lens[b]-1 of KV head h / (H/G), itself included; rows at or beyond
+ * seq_lens[b] are never read. seq_lens lives on the device and is not checked on
+ * the host: a value above T_cap is treated as T_cap, a value <= 0 yields a zero
+ * output row.
+ *
+ * Long caches are split into num_splits key ranges whose partial results are merged
+ * by a log-sum-exp combine ["GQA revolution ...", section on split-KV block
+ * computation]; that needs device scratch: opts->workspace of at least
+ * gqa_decode_workspace_size() bytes, or NULL to let the call take stream-ordered
+ * memory with hipMallocAsync/hipFreeAsync on `stream`.
+ *
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
+ * opts is required (it carries kv_capacity). D in 1..256.
+ */
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seq_lens, void *out, int B, int H, int G, int D,
+                      float scale, hipStream_t stream, const gqa_opts *opts);
+
+/*
+ * Prefill: attention of every position of a sequence over the same sequence's keys
+ * (compute-bound [GQA paper digest page, introduction and section "QA"]).
+ *
+ *   q   [B, H, T, D]   q_dtype
+ *   k   [B, G, T, D]   kv_dtype (must equal q_dtype)
+ *   v   [B, G, T, D]
+ *   out [B, H, T, D]   q_dtype
+ *
+ * causal = 1: position i attends to keys 0..i (keys above the diagonal are masked,
+ * "LLM principles -- code ...", section 3); causal = 0: to all T keys.
+ * opts may be NULL (BF16 everywhere). Supported dtypes: F32 or BF16. D in 1..256.
+ */
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, int B, int T,
+                       int H, int G, int D, float scale, int causal, hipStream_t stream,
+                       const gqa_opts *opts);
+
+/* Number of KV splits gqa_decode uses for these sizes (num_splits 0 = the library's
+ * own choice, which depends only on these arguments). Returns 0 for invalid sizes. */
+int gqa_decode_num_splits(int B, int H, int G, int D, int kv_capacity, int kv_dtype,
+                          int num_splits);
+
+/* Bytes of device workspace gqa_decode needs for these sizes; 0 when it needs none
+ * (one split). Returns SIZE_MAX for invalid sizes. */
+size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, int kv_dtype,
+                                 int num_splits);
+
+/* Static, NUL-terminated name of a status code. */
+const char *gqa_status_string(gqa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

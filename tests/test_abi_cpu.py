@@ -1,0 +1,141 @@
+"""The C ABI of libgqa.so on the host (no GPU): exported symbols, the options struct,
+status strings, the split/workspace queries, and argument validation, which runs
+before any HIP call and so can be exercised without a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_attention_decode_amd as gqa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa.h")
+FAKE = 0x10000  # never dereferenced: every case below is rejected on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gqa_decode", "gqa_prefill", "gqa_decode_workspace_size", "gqa_status_string",
+            "gqa_opts_init", "gqa_decode_num_splits"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libgqa.so does not export {n}"
+
+
+def test_opts_layout_matches_header(lib):
+    o = gqa.GqaOpts()
+    lib.gqa_opts_init(ctypes.byref(o))
+    assert o.struct_size == ctypes.sizeof(gqa.GqaOpts) == 64
+    assert (o.q_dtype, o.kv_dtype, o.kv_capacity, o.num_splits, o.path) == (1, 1, 0, 0, 0)
+    assert not o.k_scale and not o.v_scale and not o.workspace and o.workspace_bytes == 0
+
+
+def test_status_strings():
+    assert gqa.status_string(0) == "GQA_OK"
+    assert gqa.status_string(1) == "GQA_ERR_INVALID_ARG"
+    assert gqa.status_string(2) == "GQA_ERR_UNSUPPORTED"
+    assert gqa.status_string(3) == "GQA_ERR_WORKSPACE"
+    assert gqa.status_string(4) == "GQA_ERR_HIP"
+    assert gqa.status_string(99) == "GQA_ERR_UNKNOWN"
+
+
+def _decode(lib, B=2, H=8, G=2, D=128, scale=0.1, ptrs=(FAKE,) * 5, **opt):
+    fields = dict(kv_capacity=64)
+    fields.update(opt)
+    o = gqa.new_opts(**fields)
+    return lib.gqa_decode(*ptrs, B, H, G, D, scale, None, ctypes.byref(o))
+
+
+def _prefill(lib, B=1, T=16, H=8, G=2, D=128, scale=0.1, causal=1, ptrs=(FAKE,) * 4, opts=True, **opt):
+    o = gqa.new_opts(**opt)
+    return lib.gqa_prefill(*ptrs, B, T, H, G, D, scale, causal, None, ctypes.byref(o) if opts else None)
+
+
+INV, UNS, WSP = 1, 2, 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(0, FAKE, FAKE, FAKE, FAKE)), INV),
+    (dict(ptrs=(FAKE, 0, FAKE, FAKE, FAKE)), INV),
+    (dict(ptrs=(FAKE, FAKE, 0, FAKE, FAKE)), INV),
+    (dict(ptrs=(FAKE, FAKE, FAKE, 0, FAKE)), INV),
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, 0)), INV),
+    (dict(B=0), INV), (dict(H=0), INV), (dict(G=0), INV), (dict(D=0), INV),
+    (dict(H=8, G=3), INV),
+    (dict(D=257), INV),
+    (dict(kv_capacity=0), INV),
+    (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
+    (dict(num_splits=-1), INV), (dict(num_splits=1025), INV),
+    (dict(path=4), INV), (dict(path=-1), INV),
+    (dict(reserved0=1), INV),
+    (dict(q_dtype=7), INV), (dict(kv_dtype=9), INV),
+    (dict(q_dtype=0, kv_dtype=1), UNS),        # f32 q with bf16 cache
+    (dict(q_dtype=1, kv_dtype=0), UNS),
+    (dict(q_dtype=2, kv_dtype=2), UNS),        # fp8 q
+    (dict(q_dtype=0, kv_dtype=2, k_scale=FAKE, v_scale=FAKE), UNS),
+    (dict(kv_dtype=2), INV),                   # fp8 without scales
+    (dict(kv_dtype=2, k_scale=FAKE), INV),
+    (dict(q_dtype=0, kv_dtype=0, D=3, path=3), UNS),   # matrix-core path needs bf16 q and D=128
+    (dict(q_dtype=0, kv_dtype=0, D=3, path=2), UNS),   # vector path needs bf16 and D=128
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), WSP),
+    (dict(num_splits=4, workspace=FAKE + 4, workspace_bytes=1 << 30), INV),  # misaligned workspace
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_requires_opts(lib):
+    assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, None) == INV
+
+
+def test_decode_short_struct(lib):
+    o = gqa.new_opts(kv_capacity=64)
+    o.struct_size = 8
+    assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, ctypes.byref(o)) == INV
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(0, FAKE, FAKE, FAKE)), INV),
+    (dict(ptrs=(FAKE, FAKE, FAKE, 0)), INV),
+    (dict(B=0), INV), (dict(T=0), INV), (dict(H=6, G=4), INV), (dict(D=300), INV),
+    (dict(causal=2), INV), (dict(causal=-1), INV),
+    (dict(scale=float("nan")), INV),
+    (dict(q_dtype=1, kv_dtype=0), UNS),
+    (dict(q_dtype=2, kv_dtype=2), UNS),
+    (dict(path=2), UNS),                        # no vector-ALU prefill
+    (dict(q_dtype=0, kv_dtype=0, path=3), UNS), # matrix-core prefill is bf16 only
+    (dict(path=5), INV),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+
+
+def test_split_queries(lib):
+    # one split needs no workspace
+    assert gqa.decode_workspace_size(1, 4, 2, 3, 8, "f32", 1) == 0
+    assert gqa.decode_num_splits(1, 4, 2, 3, 8, "f32", 1) == 1
+    # forced split counts are honoured, even beyond the number of keys (empty splits)
+    assert gqa.decode_num_splits(2, 8, 2, 64, 10, "bf16", 7) == 7
+    assert gqa.decode_num_splits(2, 8, 2, 64, 10, "bf16", 64) == 64
+    S = 5
+    acc = 2 * 8 * S * 64 * 4
+    assert gqa.decode_workspace_size(2, 8, 2, 64, 100, "bf16", S) == ((acc + 255) // 256) * 256 + 2 * 8 * S * 2 * 4
+    # automatic choice: between 1 and the number of keys, deterministic
+    for args in [(1, 32, 8, 128, 2048, "bf16"), (16, 64, 8, 128, 4096, "bf16"), (8, 32, 1, 128, 32768, "fp8_e4m3fn"),
+                 (1, 4, 2, 3, 7, "f32")]:
+        s = gqa.decode_num_splits(*args)
+        assert 1 <= s <= args[4] and s == gqa.decode_num_splits(*args)
+    # invalid sizes
+    assert gqa.decode_num_splits(0, 8, 2, 64, 10) == 0
+    assert gqa.decode_workspace_size(1, 6, 4, 64, 10) == 2 ** 64 - 1
