@@ -1,10 +1,357 @@
-// Placeholder until the kernel lands: reports no supported shapes.
+// Wide-group GQA decode on the matrix cores (bf16 or fp8-E4M3FN KV cache, D = 128).
+//
+// With R = H/G query heads per KV head, decode does 4*R flops per cached element: at R >= 8
+// (and for MQA, R = 32, with fp8 storage) the vector ALUs cannot keep up with HBM, so both
+// contractions run as bf16 MFMA. Each KV row is read from HBM exactly once per (sequence,
+// KV head) and multiplied against all R query heads of its group inside one MFMA -- the
+// group sharing that defines GQA [GQA paper digest page (51969.com), section "Grouped-query
+// attention (GQA)"; the KV head of query head h is h / (H/G), "LLM principles -- code
+// implementation of multi-head attention (MQA and GQA)", section 5].
+//
+// Work: one workgroup (4 waves) per (sequence b, KV head g, key range). Each wave streams
+// its own 32-token blocks of the range (blocks wave, wave+4, ...), keeping an independent
+// online-softmax state; the four states are merged at the end, and a split range leaves
+// (acc, max, sum) partials for the log-sum-exp combine kernel.
+//
+// Per 32-token block, per wave:
+//   S^T (32 tokens x 16 heads per head block) = K . Q^T          -- 16x16x32 bf16 MFMA
+//        K rows go from HBM straight into the MFMA A-operand layout (16-byte loads);
+//        rows are assigned to MFMA rows so that afterwards each lane holds 8 consecutive
+//        tokens of one head, which is exactly the B-operand layout of the next product.
+//   online softmax in base 2 (scale * log2(e) * k_scale applied to the fp32 scores)
+//   O^T (128 d x 16 heads) += V^T . P^T                          -- 16x16x32 bf16 MFMA
+//        V rows are loaded coalesced (4 rows of 256 bytes per wave instruction), written to
+//        a wave-private LDS tile, and read back transposed with ds_read_b64_tr_b16
+//        (ds_read_b64_tr_b8 + exact fp8->bf16 widening for fp8).
+// Tokens at or beyond the valid length are masked by index; their rows are never loaded
+// (the load index is clamped to the last valid row, and their probabilities are zero).
+// v_scale multiplies the output once, in the epilogue.
+#include "dtypes.h"
 #include "gqa_internal.h"
+#include "mfma_util.h"
 
 namespace gqa {
 
-bool decode_mfma_supports(const AttnArgs &) { return false; }
+namespace {
 
-hipError_t launch_decode_mfma(const AttnArgs &, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlockT = 32;  // tokens per wave iteration
+constexpr int kD = 128;
+
+// MFMA row m of token sub-block `blk` (0/1) holds token tau(blk, m) of the 32-token block,
+// so that C row 4*(l/16)+i of both sub-blocks lands in lane l as tokens 8*(l/16) + 4*blk + i.
+__device__ __forceinline__ int tau(int blk, int m) { return ((m >> 2) << 3) + (blk << 2) + (m & 3); }
+
+// XOR swizzles of the 16-byte chunk position inside a V-tile row (bank-conflict avoidance
+// for the transposed reads); bf16 rows have 16 chunks, fp8 rows 8.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | (r & 8) | ((r >> 4) & 1); }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+template <bool FP8> struct Frag;
+template <> struct Frag<false> { i32x4_t k[8]; i32x4_t v[8]; };
+template <> struct Frag<true> { i32x2_t k[8]; i32x4_t v[4]; };
+
+template <bool FP8>
+__device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, const char *vbase, int t0, int ke,
+                                           int lane) {
+    constexpr int RB = FP8 ? 128 : 256;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        int row = t0 + tau(blk, lane & 15);
+        row = row < ke ? row : ke - 1;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if constexpr (FP8)
+                f.k[blk * 4 + kk] = *(const i32x2_t *)(kbase + (long)row * RB + 32 * kk + 8 * (lane >> 4));
+            else
+                f.k[blk * 4 + kk] = *(const i32x4_t *)(kbase + (long)row * RB + 64 * kk + 16 * (lane >> 4));
+        }
+    }
+    if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int row = t0 + 8 * i + (lane >> 3);
+            row = row < ke ? row : ke - 1;
+            f.v[i] = *(const i32x4_t *)(vbase + (long)row * RB + 16 * (lane & 7));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int row = t0 + 4 * i + (lane >> 4);
+            row = row < ke ? row : ke - 1;
+            f.v[i] = *(const i32x4_t *)(vbase + (long)row * RB + 16 * (lane & 15));
+        }
+    }
+}
+
+template <int NHB, bool FP8>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
+    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int VT = kBlockT * RB;                     // V tile bytes per wave
+    constexpr int HP = 16 * NHB;                         // heads padded to MFMA blocks
+    constexpr int EPI = HP * kD * 4 + HP * 4 * (kWaves + 2);
+    constexpr int LDS_BYTES = kWaves * VT > EPI ? kWaves * VT : EPI;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int S = a.num_splits;
+    const int split = blockIdx.x % S;
+    const int bg = blockIdx.x / S;
+    const int G = a.G, H = a.H, R = H / G;
+    const int b = bg / G, g = bg % G;
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
+    const int kb = split * a.split_len;
+    const int ke = kb + a.split_len < L ? kb + a.split_len : L;
+    const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
+
+    if (kb >= ke) {  // nothing to attend to in this range
+        if (S == 1) {
+            uint16_t *out = static_cast<uint16_t *>(a.out);
+            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
+        } else {
+            for (int h = threadIdx.x; h < R; h += kThreads) {
+                a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
+                a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
+            }
+        }
+        return;
+    }
+
+    // Q^T as the B operand: lane l holds Q[head 16*hb + l%16][32*kk + 8*(l/16) .. +7].
+    i32x4_t qT[NHB][4];
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + head0 * kD;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        const int h = hb * 16 + (lane & 15);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (h < R)
+                qT[hb][kk] = *(const i32x4_t *)(qp + (long)h * kD + 32 * kk + 8 * (lane >> 4));
+            else
+                qT[hb][kk] = i32x4_t{0, 0, 0, 0};
+        }
+    }
+    const float kscale = FP8 ? a.k_scale[bg] : 1.f;
+    const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+    const float c = a.scale_log2 * kscale;
+
+    const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
+    const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+    char *vt = lds + wave * VT;
+
+    f32x4_t o[NHB][8];
+    float m[NHB], lsum[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        m[hb] = -INFINITY;
+        lsum[hb] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int t0 = kb + wave * kBlockT;
+    Frag<FP8> nxt;
+    if (t0 < ke) load_block<FP8>(nxt, kbase, vbase, t0, ke, lane);
+
+    for (; t0 < ke; t0 += kWaves * kBlockT) {
+        const Frag<FP8> cur = nxt;
+        const int tn = t0 + kWaves * kBlockT;
+        if (tn < ke) load_block<FP8>(nxt, kbase, vbase, tn, ke, lane);
+
+        // V tile -> LDS (row-major, swizzled 16-byte chunks).
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 8 * i + (lane >> 3);
+                *(i32x4_t *)(vt + r * RB + 16 * ((lane & 7) ^ swz8(r))) = cur.v[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                *(i32x4_t *)(vt + r * RB + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
+            }
+        }
+
+        // S^T = K . Q^T for both 16-token sub-blocks and every head block.
+        f32x4_t s[NHB][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            i32x4_t ka[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if constexpr (FP8)
+                    ka[kk] = e4m3x8_to_bf16x8(cur.k[blk * 4 + kk]);
+                else
+                    ka[kk] = cur.k[blk * 4 + kk];
+            }
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(ka[kk], qT[hb][kk], acc);
+                s[hb][blk] = acc;
+            }
+        }
+
+        // Online softmax; lane l holds head l%16 of each head block and tokens
+        // t0 + 8*(l/16) + 4*blk + i.
+        const int tl = t0 + 8 * (lane >> 4);
+        i32x4_t pb[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            float x[8];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tl + 4 * blk + i;
+                    const float v = t < ke ? s[hb][blk][i] * c : -INFINITY;
+                    x[blk * 4 + i] = v;
+                    bm = fmaxf(bm, v);
+                }
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mn = fmaxf(m[hb], bm);
+            const float alpha = fast_exp2(m[hb] - mn);
+            float ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = fast_exp2(x[e] - mn);
+                ps += x[e];
+            }
+            lsum[hb] = lsum[hb] * alpha + ps;
+            m[hb] = mn;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                o[hb][nb][0] *= alpha;
+                o[hb][nb][1] *= alpha;
+                o[hb][nb][2] *= alpha;
+                o[hb][nb][3] *= alpha;
+            }
+            pb[hb][0] = pack_bf16_rne(x[0], x[1]);
+            pb[hb][1] = pack_bf16_rne(x[2], x[3]);
+            pb[hb][2] = pack_bf16_rne(x[4], x[5]);
+            pb[hb][3] = pack_bf16_rne(x[6], x[7]);
+        }
+
+        // O^T += V^T . P^T, 16 head dims per MFMA.
+        const int j = lane & 15, grp = lane >> 4;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            i32x4_t va;
+            if constexpr (FP8) {
+                const int r = 8 * grp + (j >> 1);
+                const i32x2_t codes = lds_read_tr8(vt + r * RB + 16 * (nb ^ swz8(r)) + 8 * (j & 1));
+                va = e4m3x8_to_bf16x8(codes);
+            } else {
+                const int r0 = 8 * grp + (j >> 2);
+                const int r1 = r0 + 4;
+                const int cc = 2 * nb + ((j & 3) >> 1);
+                const i32x2_t lo = lds_read_tr16(vt + r0 * RB + 16 * (cc ^ swz16(r0)) + 8 * (j & 1));
+                const i32x2_t hi = lds_read_tr16(vt + r1 * RB + 16 * (cc ^ swz16(r1)) + 8 * (j & 1));
+                va = i32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) o[hb][nb] = mfma16x16x32(va, pb[hb], o[hb][nb]);
+        }
+    }
+
+    // ---- merge the four waves (LDS, fixed order: deterministic) ----
+    float *O_s = reinterpret_cast<float *>(lds);     // [HP][kD]
+    float *l_s = O_s + HP * kD;                       // [HP]
+    float *M_s = l_s + HP;                            // [HP]
+    float *m_s = M_s + HP;                            // [kWaves][HP]
+    __syncthreads();  // every wave is done with its V tile
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        lsum[hb] += __shfl_xor(lsum[hb], 16);
+        lsum[hb] += __shfl_xor(lsum[hb], 32);
+        if (lane < 16) m_s[wave * HP + hb * 16 + lane] = m[hb];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        const int h = hb * 16 + (lane & 15);
+        float M = m_s[h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_s[w * HP + h]);
+        const float f = m[hb] == -INFINITY ? 0.f : fast_exp2(m[hb] - M);
+        lsum[hb] *= f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            o[hb][nb][0] *= f;
+            o[hb][nb][1] *= f;
+            o[hb][nb][2] *= f;
+            o[hb][nb][3] *= f;
+        }
+        if (wave == 0 && lane < 16) M_s[h] = M;
+    }
+    for (int w = 0; w < kWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
+                const int h = hb * 16 + (lane & 15);
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int idx = h * kD + 16 * nb + 4 * (lane >> 4) + i;
+                        O_s[idx] = (w == 0 ? 0.f : O_s[idx]) + o[hb][nb][i];
+                    }
+                if (lane < 16) l_s[h] = (w == 0 ? 0.f : l_s[h]) + lsum[hb];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (S == 1) {
+        uint16_t *out = static_cast<uint16_t *>(a.out);
+        for (int e = threadIdx.x; e < R * kD; e += kThreads) {
+            const int h = e / kD;
+            out[head0 * kD + e] = f32_to_bf16(O_s[e] / l_s[h] * vscale);
+        }
+    } else {
+        for (int e = threadIdx.x; e < R * kD; e += kThreads) {
+            const int h = e / kD, d = e % kD;
+            a.part_acc[((head0 + h) * S + split) * kD + d] = O_s[e] * vscale;
+        }
+        for (int h = threadIdx.x; h < R; h += kThreads) {
+            a.part_ml[((head0 + h) * S + split) * 2] = M_s[h];
+            a.part_ml[((head0 + h) * S + split) * 2 + 1] = l_s[h];
+        }
+    }
+}
+
+template <int NHB, bool FP8>
+hipError_t launch_nhb(const AttnArgs &a, hipStream_t stream) {
+    dim3 grid((unsigned)(a.B * a.G * a.num_splits));
+    hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_kv(const AttnArgs &a, hipStream_t stream) {
+    const int R = a.H / a.G;
+    if (R <= 16) return launch_nhb<1, FP8>(a, stream);
+    if (R <= 32) return launch_nhb<2, FP8>(a, stream);
+    return launch_nhb<4, FP8>(a, stream);
+}
+
+}  // namespace
+
+bool decode_mfma_supports(const AttnArgs &a) {
+    return a.decode && a.D == kD && a.q_dtype == DT_BF16 && (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_FP8) &&
+           a.H / a.G <= 64;
+}
+
+hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream) {
+    if (!decode_mfma_supports(a)) return hipErrorInvalidValue;
+    return a.kv_dtype == DT_FP8 ? launch_kv<true>(a, stream) : launch_kv<false>(a, stream);
+}
 
 }  // namespace gqa

@@ -1,10 +1,283 @@
-// Placeholder until the kernel lands: reports no supported shapes.
+// GQA prefill on the matrix cores (bf16, D = 128, causal or not).
+//
+// Prefill is compute-bound [GQA paper digest page (51969.com), introduction and section
+// "QA": the pre-fill stage is bound by compute, decode by loading the KV cache]. Grouping
+// does not change the flops (every query head still scores every visible key) but lets one
+// K/V tile serve all R = H/G query heads of its group [same page, section "Grouped-query
+// attention (GQA)"; the KV head of query head h is h / R, "LLM principles -- code
+// implementation of multi-head attention (MQA and GQA)", section 5]. Softmax of the scaled
+// scores with the causal mask (key j visible to row i iff j <= i) follows the same page,
+// section 3; it is evaluated online, tile by tile, in base 2.
+//
+// Work: one workgroup (8 waves, 256 query rows) per (sequence b, KV head g, position tile).
+// The 256 rows are the R heads of group g times P = 256 / R consecutive positions, so each
+// 64-key K/V tile staged in LDS is used by every head of the group. Each wave owns 32 rows
+// (one row per lane pair) and, per key tile:
+//   S^T (64 keys x 32 rows) = K . Q^T          8 + 8 MFMA 32x32x16 bf16 (K rows read from LDS
+//                                              in the A-operand layout; Q^T lives in registers)
+//   online softmax (one row per lane: row max = in-lane max + one shuffle)
+//   O^T (128 d x 32 rows) += V^T . P^T          16 MFMA 32x32x16 (V^T via ds_read_b64_tr_b16;
+//                                              P^T comes straight from the S^T registers)
+// K/V tiles are loaded with direct global->LDS 16-byte loads into two ping-pong buffers, so
+// the next tile streams in while the current one is multiplied. Causal tiles entirely above
+// the diagonal are skipped; position tiles are issued heaviest first, and the blocks of one
+// (b, g) land on one XCD (block i runs on XCD i mod 8), so its K/V stays in that XCD's L2.
+#include "dtypes.h"
 #include "gqa_internal.h"
+#include "mfma_util.h"
 
 namespace gqa {
 
-bool prefill_mfma_supports(const AttnArgs &) { return false; }
+namespace {
 
-hipError_t launch_prefill_mfma(const AttnArgs &, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;             // keys per tile
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const i32x4_t &a, const i32x4_t &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// S^T row m of a 32-key half holds key tau(m): C row 8i + 4h + j (lane half h) then covers
+// keys 16(i/2) + 8h + 4(i%2) + j, i.e. lane half h holds 8 consecutive keys per 16-key step,
+// the B-operand layout of the P.V product.
+__device__ __forceinline__ int tau(int m) {
+    const int i = m >> 3, h = (m >> 2) & 1, j = m & 3;
+    return ((i >> 1) << 4) + (h << 3) + ((i & 1) << 2) + j;
+}
+
+// XOR swizzle of the 16-byte chunk position inside a 256-byte K/V tile row.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Direct global -> LDS load of one 64-key tile of K or V (16 KB); each of the 8 waves moves
+// 2 KB (two 1 KB instructions). Lane l of instruction n fills LDS slot 64n + l: tile row
+// r = 4n + l/16, position p = l%16, which holds chunk p ^ swz(r) of key row k0 + r (clamped
+// to the last row, T-1, past the end).
+__device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k0, int T, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int n = wave * 2 + q;
+        const int r = 4 * n + (lane >> 4);
+        int key = k0 + r;
+        key = key < T ? key : T - 1;
+        const int c = (lane & 15) ^ swz(r);
+        __builtin_amdgcn_global_load_lds((const void *)(src + (long)key * kRowBytes + 16 * c),
+                                         GQA_LDS(void, lds_tile + n * 1024), 16, 0, 0);
+    }
+}
+
+template <int R>
+struct RowMap {
+    static constexpr int P = kRows / R;  // positions per workgroup
+};
+
+template <int R, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
+    constexpr int P = RowMap<R>::P;
+    __shared__ __attribute__((aligned(16))) char k_lds0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char v_lds0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char k_lds1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char v_lds1[kTileBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int T = a.Tq;
+    const int G = a.G, H = a.H;
+    const int nbg = a.B * G;
+    const int npt = (T + P - 1) / P;
+    const int bg = blockIdx.x % nbg;
+    const int pt = CAUSAL ? npt - 1 - (int)(blockIdx.x / nbg) : (int)(blockIdx.x / nbg);
+    const int b = bg / G, g = bg % G;
+    const int p0 = pt * P;
+
+    // This lane's query row.
+    const int wr = 32 * wave + (lane & 31);  // row inside the workgroup
+    const int head = g * R + wr / P;
+    const int pos = p0 + wr % P;
+    const bool row_ok = pos < T;
+    const long qrow = ((long)b * H + head) * T + (row_ok ? pos : T - 1);
+
+    // Q^T as the B operand: lane l holds Q[row][16*ks + 8*(l/32) .. +7], ks = 0..7.
+    i32x4_t qT[8];
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + qrow * kD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qT[ks] = *(const i32x4_t *)(qp + 16 * ks);
+
+    const char *kbase = static_cast<const char *>(a.k) + (long)bg * T * kRowBytes;
+    const char *vbase = static_cast<const char *>(a.v) + (long)bg * T * kRowBytes;
+
+    // Keys this workgroup needs, and the smallest position held by this wave.
+    const int wg_last = p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1;
+    const int nkt = CAUSAL ? wg_last / kBN + 1 : (T + kBN - 1) / kBN;
+    int wave_min_pos = p0 + (32 * wave) % P;  // first row of the wave
+    if (P < 32) wave_min_pos = p0;            // a wave spans several heads: all positions
+    const float c = a.scale_log2;
+
+    f32x16_t o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+
+    auto compute_tile = [&](const char *kt, const char *vt, int k0) {
+        // ---- S^T = K . Q^T for both 32-key halves ----
+        f32x16_t s[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const int r = 32 * kh + tau(lane & 31);
+            f32x16_t acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int ch = 2 * ks + (lane >> 5);
+                const i32x4_t ka = *(const i32x4_t *)(kt + r * kRowBytes + 16 * (ch ^ swz(r)));
+                acc = mfma32x32x16(ka, qT[ks], acc);
+            }
+            s[kh] = acc;
+        }
+        // ---- scale, mask, online softmax (row = lane & 31, keys per lane half) ----
+        const bool need_mask = (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > T);
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = s[kh][e] * c;
+                if (need_mask) {
+                    const int i = e >> 2, j = e & 3;
+                    const int key = k0 + 32 * kh + 16 * (i >> 1) + 8 * (lane >> 5) + 4 * (i & 1) + j;
+                    const bool vis = key < T && (!CAUSAL || key <= pos);
+                    x = vis ? x : -INFINITY;
+                }
+                s[kh][e] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m, tmax);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m - mref);
+        m = mn;
+        float ps = 0.f;
+        i32x4_t pb[4];  // P^T operands for the four 16-key steps
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(s[kh][8 * half + e] - mref);
+                    ps += p[e];
+                }
+                pb[2 * kh + half] = i32x4_t{pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3]),
+                                            pack_bf16_rne(p[4], p[5]), pack_bf16_rne(p[6], p[7])};
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        // ---- O^T += V^T . P^T ----
+        const int gq = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const int col = 32 * db + 16 * (gq & 1) + 4 * (jj & 3);  // first of 4 head dims
+                const int chn = col >> 3;
+                const int off = (col & 7) * 2;
+                const int r0 = 16 * kk + 8 * (gq >> 1) + (jj >> 2);
+                const int r1 = r0 + 4;
+                const i32x2_t lo = lds_read_tr16(vt + r0 * kRowBytes + 16 * (chn ^ swz(r0)) + off);
+                const i32x2_t hi = lds_read_tr16(vt + r1 * kRowBytes + 16 * (chn ^ swz(r1)) + off);
+                const i32x4_t va = i32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                o[db] = mfma32x32x16(va, pb[kk], o[db]);
+            }
+        }
+    };
+
+    load_tile(k_lds0, kbase, 0, T, wave, lane);
+    load_tile(v_lds0, vbase, 0, T, wave, lane);
+    wait_vmem_all();
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        if (kt + 1 < nkt) {
+            load_tile(k_lds1, kbase, (kt + 1) * kBN, T, wave, lane);
+            load_tile(v_lds1, vbase, (kt + 1) * kBN, T, wave, lane);
+        }
+        compute_tile(k_lds0, v_lds0, kt * kBN);
+        wait_vmem_all();
+        __syncthreads();
+        if (kt + 1 >= nkt) break;
+        if (kt + 2 < nkt) {
+            load_tile(k_lds0, kbase, (kt + 2) * kBN, T, wave, lane);
+            load_tile(v_lds0, vbase, (kt + 2) * kBN, T, wave, lane);
+        }
+        compute_tile(k_lds1, v_lds1, (kt + 1) * kBN);
+        wait_vmem_all();
+        __syncthreads();
+    }
+
+    // ---- epilogue: out[row][d] = O^T[d][row] / l ----
+    lsum += __shfl_xor(lsum, 32);
+    if (row_ok) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t *op = static_cast<uint16_t *>(a.out) + qrow * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = 32 * db + 8 * i + 4 * (lane >> 5);
+                i32x2_t w;
+                w[0] = pack_bf16_rne(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+                w[1] = pack_bf16_rne(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+                *(i32x2_t *)(op + d) = w;
+            }
+    }
+}
+
+template <int R>
+hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
+    constexpr int P = RowMap<R>::P;
+    const int npt = (a.Tq + P - 1) / P;
+    dim3 grid((unsigned)(a.B * a.G * npt));
+    if (a.causal)
+        hipLaunchKernelGGL((prefill_mfma_kernel<R, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<R, false>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_mfma_supports(const AttnArgs &a) {
+    if (a.decode || a.D != kD || a.q_dtype != DT_BF16 || a.kv_dtype != DT_BF16) return false;
+    const int R = a.H / a.G;
+    return R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32 || R == 64;
+}
+
+hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream) {
+    if (!prefill_mfma_supports(a)) return hipErrorInvalidValue;
+    switch (a.H / a.G) {
+        case 1: return launch_r<1>(a, stream);
+        case 2: return launch_r<2>(a, stream);
+        case 4: return launch_r<4>(a, stream);
+        case 8: return launch_r<8>(a, stream);
+        case 16: return launch_r<16>(a, stream);
+        case 32: return launch_r<32>(a, stream);
+        default: return launch_r<64>(a, stream);
+    }
+}
 
 }  // namespace gqa
