@@ -59,12 +59,14 @@ __device__ __forceinline__ i32x4_t e4m3x8_to_bf16x8(i32x2_t c) {
     return r;
 }
 
-// Round-to-nearest-even packing of two binary32 values into a bf16 pair.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even packing of two binary32 values into a bf16 pair
+// (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ int pack_bf16_rne(float lo, float hi) {
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    a += 0x7fffu + ((a >> 16) & 1u);
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (int)__builtin_amdgcn_perm(b, a, 0x07060302u);
+    const f32x2v_t v = {lo, hi};
+    return __builtin_bit_cast(int, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -9,19 +9,23 @@
 // scores with the causal mask (key j visible to row i iff j <= i) follows the same page,
 // section 3; it is evaluated online, tile by tile, in base 2.
 //
-// Work: one workgroup (8 waves, 256 query rows) per (sequence b, KV head g, position tile).
-// The 256 rows are the R heads of group g times P = 256 / R consecutive positions, so each
-// 64-key K/V tile staged in LDS is used by every head of the group. Each wave owns 32 rows
-// (one row per lane pair) and, per key tile:
-//   S^T (64 keys x 32 rows) = K . Q^T          8 + 8 MFMA 32x32x16 bf16 (K rows read from LDS
-//                                              in the A-operand layout; Q^T lives in registers)
-//   online softmax (one row per lane: row max = in-lane max + one shuffle)
+// Work: one workgroup (4 waves, 128 query rows) per (sequence b, KV head g, position
+// tile); two workgroups share a CU, so one's softmax overlaps the other's MFMAs. The 128
+// rows are the R heads of group g times P = 128 / R consecutive positions, so each 64-key
+// K/V tile staged in LDS is used by every head of the group. Each wave owns 32 rows (lane l
+// and lane l+32 hold row l%32) and, per key tile:
+//   S^T (64 keys x 32 rows) = K . Q^T          16 MFMA 32x32x16 bf16 (K rows read from LDS
+//                                              in the A-operand layout; Q^T stays in registers)
+//   online softmax, one row per lane: the row max is an in-lane max plus one shuffle
 //   O^T (128 d x 32 rows) += V^T . P^T          16 MFMA 32x32x16 (V^T via ds_read_b64_tr_b16;
 //                                              P^T comes straight from the S^T registers)
+// The softmax keeps a per-row reference max and rescales O only when a row's running max
+// exceeds it by more than 8 (base 2), so every probability stays below 2^8 and most tiles
+// skip the rescale; the result is the same softmax, since the reference cancels in O / l.
 // K/V tiles are loaded with direct global->LDS 16-byte loads into two ping-pong buffers, so
 // the next tile streams in while the current one is multiplied. Causal tiles entirely above
-// the diagonal are skipped; position tiles are issued heaviest first, and the blocks of one
-// (b, g) land on one XCD (block i runs on XCD i mod 8), so its K/V stays in that XCD's L2.
+// the diagonal are skipped; position tiles are issued heaviest first, and all blocks of one
+// (b, g) land on one XCD (block i runs on XCD i mod 8), so its K/V stays in that L2.
 #include "dtypes.h"
 #include "gqa_internal.h"
 #include "mfma_util.h"
@@ -30,13 +34,14 @@ namespace gqa {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;             // keys per tile
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+constexpr float kRescaleSlack = 8.f;         // base-2 headroom before O is rescaled
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
@@ -53,19 +58,21 @@ __device__ __forceinline__ int tau(int m) {
     return ((i >> 1) << 4) + (h << 3) + ((i & 1) << 2) + j;
 }
 
-// XOR swizzle of the 16-byte chunk position inside a 256-byte K/V tile row.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// XOR swizzle of the 16-byte chunk position inside a 256-byte K/V tile row. Measured on
+// gfx950 (SQ_LDS_BANK_CONFLICT) to be conflict-free for both read patterns below: the
+// ds_read_b128 K-operand reads and the ds_read_b64_tr_b16 V-operand reads.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// Direct global -> LDS load of one 64-key tile of K or V (16 KB); each of the 8 waves moves
-// 2 KB (two 1 KB instructions). Lane l of instruction n fills LDS slot 64n + l: tile row
+// Direct global -> LDS load of one 64-key tile of K or V (16 KB); each of the 4 waves moves
+// 4 KB (four 1 KB instructions). Lane l of instruction n fills LDS slot 64n + l: tile row
 // r = 4n + l/16, position p = l%16, which holds chunk p ^ swz(r) of key row k0 + r (clamped
 // to the last row, T-1, past the end).
 __device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k0, int T, int wave, int lane) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int n = wave * 2 + q;
+    for (int q = 0; q < 4; ++q) {
+        const int n = wave * 4 + q;
         const int r = 4 * n + (lane >> 4);
         int key = k0 + r;
         key = key < T ? key : T - 1;
@@ -75,21 +82,16 @@ __device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k
     }
 }
 
-template <int R>
-struct RowMap {
-    static constexpr int P = kRows / R;  // positions per workgroup
-};
-
 template <int R, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
-    constexpr int P = RowMap<R>::P;
+__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
+    constexpr int P = kRows / R;  // positions per workgroup
     __shared__ __attribute__((aligned(16))) char k_lds0[kTileBytes];
     __shared__ __attribute__((aligned(16))) char v_lds0[kTileBytes];
     __shared__ __attribute__((aligned(16))) char k_lds1[kTileBytes];
     __shared__ __attribute__((aligned(16))) char v_lds1[kTileBytes];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int T = a.Tq;
     const int G = a.G, H = a.H;
     const int nbg = a.B * G;
@@ -106,11 +108,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
     const bool row_ok = pos < T;
     const long qrow = ((long)b * H + head) * T + (row_ok ? pos : T - 1);
 
+    // Base-2 score scale; a negative scale is folded into Q so that c > 0 and the row max
+    // can be taken on the raw scores.
+    float c = a.scale_log2;
+    const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
+    c = fmaxf(fabsf(c), 1e-30f);  // a zero scale stays (numerically) uniform, without 0 * -inf
+
     // Q^T as the B operand: lane l holds Q[row][16*ks + 8*(l/32) .. +7], ks = 0..7.
     i32x4_t qT[8];
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + qrow * kD + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qT[ks] = *(const i32x4_t *)(qp + 16 * ks);
+    for (int ks = 0; ks < 8; ++ks) {
+        qT[ks] = *(const i32x4_t *)(qp + 16 * ks);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qT[ks][e] ^= qsign;
+    }
 
     const char *kbase = static_cast<const char *>(a.k) + (long)bg * T * kRowBytes;
     const char *vbase = static_cast<const char *>(a.v) + (long)bg * T * kRowBytes;
@@ -118,56 +130,71 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
     // Keys this workgroup needs, and the smallest position held by this wave.
     const int wg_last = p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1;
     const int nkt = CAUSAL ? wg_last / kBN + 1 : (T + kBN - 1) / kBN;
-    int wave_min_pos = p0 + (32 * wave) % P;  // first row of the wave
-    if (P < 32) wave_min_pos = p0;            // a wave spans several heads: all positions
-    const float c = a.scale_log2;
+    const int wave_min_pos = P >= 32 ? p0 + (32 * wave) % P : p0;
 
     f32x16_t o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-    float m = -INFINITY, lsum = 0.f;
+    float mref = -INFINITY, lsum = 0.f;
 
-    auto compute_tile = [&](const char *kt, const char *vt, int k0) {
-        // ---- S^T = K . Q^T for both 32-key halves ----
+    // Per-lane constant parts of the LDS addresses.
+    const int hl = lane >> 5;
+    int kaddr[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) kaddr[kh] = (32 * kh + tau(lane & 31));
+    const int gq = lane >> 4, jj = lane & 15;
+    const int vrow0 = 8 * (gq >> 1) + (jj >> 2);                    // + 16 kk (+4 for the upper half)
+    const int vcol = 16 * (gq & 1) + 4 * (jj & 3);                  // + 32 db
+    const int voff = (vcol & 7) * 2;
+
+    auto compute_tile = [&](const char *kt, const char *vt, int k0, bool need_mask) {
+        // ---- S^T = K . Q^T; the two 32-key halves accumulate independently, so
+        // consecutive MFMAs never wait on each other ----
         f32x16_t s[2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const int r = 32 * kh + tau(lane & 31);
-            f32x16_t acc;
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+            for (int e = 0; e < 16; ++e) s[kh][e] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int ch = 2 * ks + (lane >> 5);
-                const i32x4_t ka = *(const i32x4_t *)(kt + r * kRowBytes + 16 * (ch ^ swz(r)));
-                acc = mfma32x32x16(ka, qT[ks], acc);
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const int r = kaddr[kh];
+                const i32x4_t ka = *(const i32x4_t *)(kt + r * kRowBytes + 16 * ((2 * ks + hl) ^ swz(r)));
+                s[kh] = mfma32x32x16(ka, qT[ks], s[kh]);
             }
-            s[kh] = acc;
+        // ---- mask (diagonal / tail tiles only) and tile max on the raw scores ----
+        if (need_mask) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = e >> 2, j = e & 3;
+                    const int key = k0 + 32 * kh + 16 * (i >> 1) + 8 * hl + 4 * (i & 1) + j;
+                    const bool vis = key < T && (!CAUSAL || key <= pos);
+                    s[kh][e] = vis ? s[kh][e] : -INFINITY;
+                }
         }
-        // ---- scale, mask, online softmax (row = lane & 31, keys per lane half) ----
-        const bool need_mask = (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > T);
         float tmax = -INFINITY;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float x = s[kh][e] * c;
-                if (need_mask) {
-                    const int i = e >> 2, j = e & 3;
-                    const int key = k0 + 32 * kh + 16 * (i >> 1) + 8 * (lane >> 5) + 4 * (i & 1) + j;
-                    const bool vis = key < T && (!CAUSAL || key <= pos);
-                    x = vis ? x : -INFINITY;
-                }
-                s[kh][e] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m, tmax);
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m - mref);
-        m = mn;
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kh][e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
+        // ---- lazy rescale: move the reference only when the max outgrows it by > 2^8 ----
+        if (__any(tmax > mref + kRescaleSlack)) {
+            const float mn = fmaxf(mref, tmax);
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(mref - mn);
+            mref = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        }
+        const float nref = mref == -INFINITY ? 0.f : -mref;
         float ps = 0.f;
         i32x4_t pb[4];  // P^T operands for the four 16-key steps
 #pragma unroll
@@ -177,34 +204,33 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
                 float p[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    p[e] = fast_exp2(s[kh][8 * half + e] - mref);
+                    p[e] = fast_exp2(fmaf(s[kh][8 * half + e], c, nref));
                     ps += p[e];
                 }
                 pb[2 * kh + half] = i32x4_t{pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3]),
                                             pack_bf16_rne(p[4], p[5]), pack_bf16_rne(p[6], p[7])};
             }
-        lsum = lsum * alpha + ps;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        lsum += ps;
         // ---- O^T += V^T . P^T ----
-        const int gq = lane >> 4, jj = lane & 15;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            const int r0 = 16 * kk + vrow0;
+            const int r1 = r0 + 4;
+            const char *v0 = vt + r0 * kRowBytes + voff;
+            const char *v1 = vt + r1 * kRowBytes + voff;
+            const int s0 = swz(r0), s1 = swz(r1);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                const int col = 32 * db + 16 * (gq & 1) + 4 * (jj & 3);  // first of 4 head dims
-                const int chn = col >> 3;
-                const int off = (col & 7) * 2;
-                const int r0 = 16 * kk + 8 * (gq >> 1) + (jj >> 2);
-                const int r1 = r0 + 4;
-                const i32x2_t lo = lds_read_tr16(vt + r0 * kRowBytes + 16 * (chn ^ swz(r0)) + off);
-                const i32x2_t hi = lds_read_tr16(vt + r1 * kRowBytes + 16 * (chn ^ swz(r1)) + off);
-                const i32x4_t va = i32x4_t{lo[0], lo[1], hi[0], hi[1]};
-                o[db] = mfma32x32x16(va, pb[kk], o[db]);
+                const int chn = (32 * db + vcol) >> 3;
+                const i32x2_t lo = lds_read_tr16(v0 + 16 * (chn ^ s0));
+                const i32x2_t hi = lds_read_tr16(v1 + 16 * (chn ^ s1));
+                o[db] = mfma32x32x16(i32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kk], o[db]);
             }
         }
+    };
+
+    auto tile_needs_mask = [&](int k0) {
+        return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > T);
     };
 
     load_tile(k_lds0, kbase, 0, T, wave, lane);
@@ -216,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
             load_tile(k_lds1, kbase, (kt + 1) * kBN, T, wave, lane);
             load_tile(v_lds1, vbase, (kt + 1) * kBN, T, wave, lane);
         }
-        compute_tile(k_lds0, v_lds0, kt * kBN);
+        compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
         wait_vmem_all();
         __syncthreads();
         if (kt + 1 >= nkt) break;
@@ -224,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
             load_tile(k_lds0, kbase, (kt + 2) * kBN, T, wave, lane);
             load_tile(v_lds0, vbase, (kt + 2) * kBN, T, wave, lane);
         }
-        compute_tile(k_lds1, v_lds1, (kt + 1) * kBN);
+        compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
         wait_vmem_all();
         __syncthreads();
     }
@@ -238,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d = 32 * db + 8 * i + 4 * (lane >> 5);
+                const int d = 32 * db + 8 * i + 4 * hl;
                 i32x2_t w;
                 w[0] = pack_bf16_rne(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
                 w[1] = pack_bf16_rne(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a) {
 
 template <int R>
 hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
-    constexpr int P = RowMap<R>::P;
+    constexpr int P = kRows / R;
     const int npt = (a.Tq + P - 1) / P;
     dim3 grid((unsigned)(a.B * a.G * npt));
     if (a.causal)
