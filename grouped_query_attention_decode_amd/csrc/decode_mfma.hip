@@ -50,7 +50,7 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 template <bool FP8> struct Frag;
 template <> struct Frag<false> { i32x4_t k[8]; i32x4_t v[8]; };
-template <> struct Frag<true> { i32x2_t k[8]; i32x4_t v[4]; };
+template <> struct Frag<true> { i32x4_t k[4]; i32x4_t v[4]; };
 
 template <bool FP8>
 __device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, const char *vbase, int t0, int ke,
@@ -60,11 +60,14 @@ __device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, cons
     for (int blk = 0; blk < 2; ++blk) {
         int row = t0 + tau(blk, lane & 15);
         row = row < ke ? row : ke - 1;
+        if constexpr (FP8) {
+            // 16 fp8 per lane: head dims 64p + 16*(l/16) .. +15 feed k-steps 2p and 2p+1.
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if constexpr (FP8)
-                f.k[blk * 4 + kk] = *(const i32x2_t *)(kbase + (long)row * RB + 32 * kk + 8 * (lane >> 4));
-            else
+            for (int p = 0; p < 2; ++p)
+                f.k[blk * 2 + p] = *(const i32x4_t *)(kbase + (long)row * RB + 64 * p + 16 * (lane >> 4));
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
                 f.k[blk * 4 + kk] = *(const i32x4_t *)(kbase + (long)row * RB + 64 * kk + 16 * (lane >> 4));
         }
     }
@@ -96,9 +99,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    // Split-major order: the blocks resident on one CU at once are far apart in the grid and
+    // so pair long (early) key ranges with short or empty (late) ones of ragged batches.
     const int S = a.num_splits;
-    const int split = blockIdx.x % S;
-    const int bg = blockIdx.x / S;
+    const int nbg = a.B * a.G;
+    const int split = blockIdx.x / nbg;
+    const int bg = blockIdx.x % nbg;
     const int G = a.G, H = a.H, R = H / G;
     const int b = bg / G, g = bg % G;
     int L = a.seq_lens[b];
@@ -128,8 +134,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
         const int h = hb * 16 + (lane & 15);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            // k-step kk covers head dims dk(kk) .. +7 of this lane; fp8 pairs the steps so
+            // that one 16-byte K load serves two of them (the same order on both operands).
+            const int dk = FP8 ? 64 * (kk >> 1) + 16 * (lane >> 4) + 8 * (kk & 1) : 32 * kk + 8 * (lane >> 4);
             if (h < R)
-                qT[hb][kk] = *(const i32x4_t *)(qp + (long)h * kD + 32 * kk + 8 * (lane >> 4));
+                qT[hb][kk] = *(const i32x4_t *)(qp + (long)h * kD + dk);
             else
                 qT[hb][kk] = i32x4_t{0, 0, 0, 0};
         }
@@ -158,10 +167,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
 
     for (; t0 < ke; t0 += kWaves * kBlockT) {
         const Frag<FP8> cur = nxt;
-        const int tn = t0 + kWaves * kBlockT;
-        if (tn < ke) load_block<FP8>(nxt, kbase, vbase, tn, ke, lane);
-
-        // V tile -> LDS (row-major, swizzled 16-byte chunks).
+        // V tile -> LDS (row-major, swizzled 16-byte chunks) first, so the V registers are
+        // free again before the next block's loads are issued.
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -175,6 +182,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
                 *(i32x4_t *)(vt + r * RB + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
             }
         }
+        // Prefetch the next block before this block's work. The load is unconditional and
+        // branch-free (past the end it re-reads the current block, which the cache holds),
+        // and the barrier keeps the scheduler from sinking it next to its use -- otherwise
+        // every block waits out a full memory latency.
+        const int tn = t0 + kWaves * kBlockT < ke ? t0 + kWaves * kBlockT : t0;
+        load_block<FP8>(nxt, kbase, vbase, tn, ke, lane);
+        __builtin_amdgcn_sched_barrier(0);
 
         // S^T = K . Q^T for both 16-token sub-blocks and every head block.
         f32x4_t s[NHB][2];
@@ -183,10 +197,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
             i32x4_t ka[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                if constexpr (FP8)
-                    ka[kk] = e4m3x8_to_bf16x8(cur.k[blk * 4 + kk]);
-                else
+                if constexpr (FP8) {
+                    const i32x4_t w = cur.k[blk * 2 + (kk >> 1)];
+                    ka[kk] = e4m3x8_to_bf16x8((kk & 1) ? i32x2_t{w[2], w[3]} : i32x2_t{w[0], w[1]});
+                } else {
                     ka[kk] = cur.k[blk * 4 + kk];
+                }
             }
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) {

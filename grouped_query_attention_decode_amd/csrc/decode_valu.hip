@@ -48,9 +48,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(AttnArgs a) {
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;    // row group inside the wave
     const int chunk = lane & 15;  // 8 head dims: 8*chunk .. 8*chunk+7
+    // Split-major block order (see decode_mfma.hip).
     const int S = a.num_splits;
-    const int split = blockIdx.x % S;
-    const int bg = blockIdx.x / S;
+    const int split = blockIdx.x / (a.B * a.G);
+    const int bg = blockIdx.x % (a.B * a.G);
     const int G = a.G, H = a.H, R = H / G;
     const int b = bg / G, g = bg % G;
     int L = a.seq_lens[b];
@@ -120,7 +121,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(AttnArgs a) {
             kc[i] = kn[i];
             vc[i] = vn[i];
         }
-        if (t0 + kWaves * kRows < ke) load(t0 + kWaves * kRows);
+        // Unconditional, branch-free prefetch of the next tile (past the end it re-reads this
+        // tile from cache), pinned ahead of this tile's work.
+        load(t0 + kWaves * kRows < ke ? t0 + kWaves * kRows : t0);
+        __builtin_amdgcn_sched_barrier(0);
 
         float s[8][RP], mx[RP];
 #pragma unroll
