@@ -11,8 +11,10 @@ B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown".
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations. Each step reads the next of several replicas of its inputs, together
 at least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set and the
-figures are HBM figures. HIP events recorded on the launch stream around every call
-give the per-launch duration used for the roofline.
+figures are HBM figures. The K timed steps are captured once into a HIP graph and
+replayed, so the host's launch cost does not idle the GPU; HIP events on the launch
+stream around the replay give the per-step (= per-launch) duration used for the
+roofline. The eager, host-launched per-call time is reported beside it.
 
 Prints one JSON line.
 """
@@ -117,27 +119,66 @@ def make_prefill_runner(gqa, c: W.PrefillCase, dev):
     return step, nrep, out
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, graph=True):
+    """Time exactly `steps` calls of `step` after `warmup` untimed calls.
+
+    With graph=True the timed calls are captured once into a HIP graph (each call still
+    reads its own input replica) and the graph is replayed between two device
+    synchronisations, so host-side launch cost does not leave the GPU idle; HIP events on
+    the launch stream bracket the replay. Returns per-step figures in milliseconds, plus the
+    eager (host-launched) per-call time for reference.
+    """
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record()
-    for i in range(steps):
-        starts[i].record()
+    # Eager per-call time (host launch cost included), for reference.
+    n_eager = min(steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_eager):
         step()
-        ends[i].record()
-    t_end.record()
+    e1.record()
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return {"ms_per_step": total_ms / steps, "launch_ms_mean": sum(per) / len(per),
-            "launch_ms_median": per[len(per) // 2], "launch_ms_p10": per[len(per) // 10],
-            "launch_ms_p90": per[(9 * len(per)) // 10]}
+    eager_ms = e0.elapsed_time(e1) / n_eager
+    res = {"eager_ms_per_call": eager_ms}
+    if graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(steps):
+                    step()
+        torch.cuda.synchronize()
+        g.replay()  # untimed replay: graph upload, first-touch effects
+        torch.cuda.synchronize()
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            t_begin.record(stream)
+            g.replay()
+            t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        res.update({"ms_per_step": total_ms / steps, "launch_ms_mean": total_ms / steps, "timing": "hip_graph"})
+        del g
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_begin.record()
+        for i in range(steps):
+            starts[i].record()
+            step()
+            ends[i].record()
+        t_end.record()
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        per = sorted(st.elapsed_time(en) for st, en in zip(starts, ends))
+        res.update({"ms_per_step": total_ms / steps, "launch_ms_mean": sum(per) / len(per), "timing": "eager"})
+    return res
 
 
 def bench_decode(gqa, c, steps, warmup, dev):
@@ -154,8 +195,7 @@ def bench_decode(gqa, c, steps, warmup, dev):
         "kv_bytes": by["kv"], "algorithmic_bytes": by["total"], "flops": decode_flops(c),
         "kv_read_GBps": by["kv"] / s / 1e9, "tok_per_s": c.B / s,
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
-        "launch_us_median": t["launch_ms_median"] * 1e3, "launch_us_p10": t["launch_ms_p10"] * 1e3,
-        "launch_us_p90": t["launch_ms_p90"] * 1e3, "replicas": nrep,
+        "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None},
     }
@@ -172,7 +212,7 @@ def bench_prefill(gqa, c, steps, warmup, dev):
         "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T": c.T, "causal": c.causal,
         "flops": fl, "algorithmic_bytes": prefill_bytes(c), "tflops": fl / s / 1e12,
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
-        "launch_us_median": t["launch_ms_median"] * 1e3, "replicas": nrep,
+        "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
     }
