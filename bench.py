@@ -40,12 +40,41 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 COLD_BYTES = 1 << 30            # replicas rotate through at least this much memory
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "grouped_query_attention_decode_amd", "csrc")
+
 HEADLINE = "llama7b_gqa8_decode_L2048"
 METRIC = "GQA decode KV-read GB/s (% HBM peak) + tok/s; prefill TFLOP/s (% MFMA peak)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of every kernel source; counters taken on other sources do not apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from recorded FETCH_SIZE/WRITE_SIZE counters, scaled by the same
+    counters on a plain copy of known size; None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("traffic_bytes_per_launch")
 
 
 # ------------------------------------------------------------------------------------
@@ -197,7 +226,7 @@ def bench_decode(gqa, c, steps, warmup, dev):
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(c.name)},
     }
 
 
@@ -214,7 +243,7 @@ def bench_prefill(gqa, c, steps, warmup, dev):
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(c.name)},
     }
 
 
@@ -251,20 +280,32 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=[k for k in W.WORKLOADS if k != "toy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter reference)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(use --gpus 1)", file=sys.stderr)
+        print("bench.py measures a single GPU; the multi-GPU path is not implemented "
+              "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    import grouped_query_attention_decode_amd as gqa
-    gqa.library()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "copies": 5}))
+        return
+
+    import grouped_query_attention_decode_amd as gqa
+    gqa.library()
 
     def run(name, steps, warmup):
         case = W.WORKLOADS[name](0)
