@@ -143,7 +143,11 @@ def _stream_handle(stream, device) -> int:
 
 def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
            num_splits=0, path="auto", workspace=None, stream=None):
-    """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype)."""
+    """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype).
+
+    ``workspace`` (uint8 device tensor of at least ``decode_workspace_size`` bytes) must be
+    zero-filled before its first use; each completed call leaves it ready for the next.
+    Without one, a zeroed workspace is allocated for this call."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
         _need_cuda(t, n)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
@@ -173,7 +177,7 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
     need = decode_workspace_size(B, H, G, D, T_cap, kv_code, int(num_splits))
     if need > 0:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         o.workspace, o.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = library().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                               out.data_ptr(), B, H, G, D, float(scale), _stream_handle(stream, q.device),

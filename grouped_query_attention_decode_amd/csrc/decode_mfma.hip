@@ -29,6 +29,7 @@
 #include "dtypes.h"
 #include "gqa_internal.h"
 #include "mfma_util.h"
+#include "splitkv.h"
 
 namespace gqa {
 
@@ -93,9 +94,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int VT = kBlockT * RB;                     // V tile bytes per wave
     constexpr int HP = 16 * NHB;                         // heads padded to MFMA blocks
-    constexpr int EPI = HP * kD * 4 + HP * 4 * (kWaves + 2);
+    constexpr int EPI = kWaves * HP * kD * 4;            // per-wave accumulator slices
     constexpr int LDS_BYTES = kWaves * VT > EPI ? kWaves * VT : EPI;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -107,26 +109,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     const int bg = blockIdx.x % nbg;
     const int G = a.G, H = a.H, R = H / G;
     const int b = bg / G, g = bg % G;
-    int L = a.seq_lens[b];
-    L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
     const int kb = split * a.split_len;
-    const int ke = kb + a.split_len < L ? kb + a.split_len : L;
     const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
 
-    if (kb >= ke) {  // nothing to attend to in this range
-        if (S == 1) {
-            uint16_t *out = static_cast<uint16_t *>(a.out);
-            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
-        } else {
-            for (int h = threadIdx.x; h < R; h += kThreads) {
-                a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
-                a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
-            }
-        }
-        return;
-    }
-
-    // Q^T as the B operand: lane l holds Q[head 16*hb + l%16][32*kk + 8*(l/16) .. +7].
+    // Q^T as the B operand: lane l holds Q[head 16*hb + l%16][32*kk + 8*(l/16) .. +7]. The query,
+    // the scales and this wave's first block do not depend on the length (the block's rows are
+    // clamped to the allocation), so they are requested before it and share its round trip.
     i32x4_t qT[NHB][4];
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + head0 * kD;
 #pragma unroll
@@ -137,18 +125,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
             // k-step kk covers head dims dk(kk) .. +7 of this lane; fp8 pairs the steps so
             // that one 16-byte K load serves two of them (the same order on both operands).
             const int dk = FP8 ? 64 * (kk >> 1) + 16 * (lane >> 4) + 8 * (kk & 1) : 32 * kk + 8 * (lane >> 4);
-            if (h < R)
-                qT[hb][kk] = *(const i32x4_t *)(qp + (long)h * kD + dk);
-            else
-                qT[hb][kk] = i32x4_t{0, 0, 0, 0};
+            qT[hb][kk] = *(const i32x4_t *)(qp + (long)(h < R ? h : R - 1) * kD + dk);
         }
     }
     const float kscale = FP8 ? a.k_scale[bg] : 1.f;
     const float vscale = FP8 ? a.v_scale[bg] : 1.f;
-    const float c = a.scale_log2 * kscale;
 
     const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
     const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+    int t0 = kb + wave * kBlockT;
+    Frag<FP8> nxt;
+    if (t0 < a.Tk) load_block<FP8>(nxt, kbase, vbase, t0, a.Tk, lane);
+
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
+    const int ke = kb + a.split_len < L ? kb + a.split_len : L;
+
+    if (kb >= ke) {  // nothing to attend to in this range
+        // Fused merges count only non-empty ranges, so an empty one only has to produce the
+        // zero row of an empty sequence.
+        if (S == 1 || (a.fuse_combine && L == 0 && split == 0)) {
+            uint16_t *out = static_cast<uint16_t *>(a.out);
+            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
+        } else if (!a.fuse_combine) {
+            for (int h = threadIdx.x; h < R; h += kThreads) {
+                a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
+                a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+        if (hb * 16 + (lane & 15) >= R)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qT[hb][kk] = i32x4_t{0, 0, 0, 0};
+    const float c = a.scale_log2 * kscale;
     char *vt = lds + wave * VT;
 
     f32x4_t o[NHB][8];
@@ -161,12 +173,22 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
         for (int nb = 0; nb < 8; ++nb) o[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    int t0 = kb + wave * kBlockT;
-    Frag<FP8> nxt;
-    if (t0 < ke) load_block<FP8>(nxt, kbase, vbase, t0, ke, lane);
-
     for (; t0 < ke; t0 += kWaves * kBlockT) {
-        const Frag<FP8> cur = nxt;
+        Frag<FP8> cur = nxt;
+        // Only a first block (requested before the length was known) can hold rows at or past
+        // the end; they may contain anything, NaN included. Their scores are masked by index
+        // below; zero their values so that the zero probabilities stay exact.
+        if (t0 + kBlockT > ke) {
+            if constexpr (FP8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 8 * i + (lane >> 3) >= ke) cur.v[i] = i32x4_t{0, 0, 0, 0};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (t0 + 4 * i + (lane >> 4) >= ke) cur.v[i] = i32x4_t{0, 0, 0, 0};
+            }
+        }
         // V tile -> LDS (row-major, swizzled 16-byte chunks) first, so the V registers are
         // free again before the next block's loads are issued.
         if constexpr (FP8) {
@@ -277,69 +299,70 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
         }
     }
 
-    // ---- merge the four waves (LDS, fixed order: deterministic) ----
-    float *O_s = reinterpret_cast<float *>(lds);     // [HP][kD]
-    float *l_s = O_s + HP * kD;                       // [HP]
-    float *M_s = l_s + HP;                            // [HP]
-    float *m_s = M_s + HP;                            // [kWaves][HP]
+    // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
+    // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
+    // slice; every thread then sums four slices for 4 consecutive head dims.
+    float *o_w = reinterpret_cast<float *>(lds);  // [kWaves][HP][kD]
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         lsum[hb] += __shfl_xor(lsum[hb], 16);
         lsum[hb] += __shfl_xor(lsum[hb], 32);
-        if (lane < 16) m_s[wave * HP + hb * 16 + lane] = m[hb];
+        if (lane < 16) m_w[wave][hb * 16 + lane] = m[hb];
     }
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         const int h = hb * 16 + (lane & 15);
-        float M = m_s[h];
+        if (hb * 16 < R) {
+            float M = m_w[0][h];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_s[w * HP + h]);
-        const float f = m[hb] == -INFINITY ? 0.f : fast_exp2(m[hb] - M);
-        lsum[hb] *= f;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            o[hb][nb][0] *= f;
-            o[hb][nb][1] *= f;
-            o[hb][nb][2] *= f;
-            o[hb][nb][3] *= f;
-        }
-        if (wave == 0 && lane < 16) M_s[h] = M;
-    }
-    for (int w = 0; w < kWaves; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int hb = 0; hb < NHB; ++hb) {
-                const int h = hb * 16 + (lane & 15);
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
+            const float f = m[hb] == -INFINITY ? 0.f : fast_exp2(m[hb] - M);
+            if (h < R) {
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int idx = h * kD + 16 * nb + 4 * (lane >> 4) + i;
-                        O_s[idx] = (w == 0 ? 0.f : O_s[idx]) + o[hb][nb][i];
-                    }
-                if (lane < 16) l_s[h] = (w == 0 ? 0.f : l_s[h]) + lsum[hb];
+                    *(f32x4_t *)&o_w[(wave * HP + h) * kD + 16 * nb + 4 * (lane >> 4)] =
+                        f32x4_t{o[hb][nb][0] * f, o[hb][nb][1] * f, o[hb][nb][2] * f, o[hb][nb][3] * f};
+                if (lane < 16) l_w[wave][h] = lsum[hb] * f;
             }
         }
-        __syncthreads();
     }
-
-    if (S == 1) {
-        uint16_t *out = static_cast<uint16_t *>(a.out);
-        for (int e = threadIdx.x; e < R * kD; e += kThreads) {
-            const int h = e / kD;
-            out[head0 * kD + e] = f32_to_bf16(O_s[e] / l_s[h] * vscale);
+    __syncthreads();
+    for (int cidx = threadIdx.x; cidx < R * (kD / 4); cidx += kThreads) {
+        const int h = cidx / (kD / 4), d = 4 * (cidx % (kD / 4));
+        f32x4_t acc = *(const f32x4_t *)&o_w[h * kD + d];
+        float l = l_w[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            const f32x4_t x = *(const f32x4_t *)&o_w[(w * HP + h) * kD + d];
+            acc[0] += x[0];
+            acc[1] += x[1];
+            acc[2] += x[2];
+            acc[3] += x[3];
+            l += l_w[w][h];
         }
-    } else {
-        for (int e = threadIdx.x; e < R * kD; e += kThreads) {
-            const int h = e / kD, d = e % kD;
-            a.part_acc[((head0 + h) * S + split) * kD + d] = O_s[e] * vscale;
+        if (S == 1) {
+            const float inv = vscale / l;
+            uint16_t *out = static_cast<uint16_t *>(a.out) + (head0 + h) * kD + d;
+            *(i32x2_t *)out = i32x2_t{pack_bf16_rne(acc[0] * inv, acc[1] * inv), pack_bf16_rne(acc[2] * inv, acc[3] * inv)};
+        } else {
+            float *pa = &a.part_acc[((head0 + h) * S + split) * kD + d];
+            splitkv_store4(pa, f32x4_t{acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale},
+                           a.fuse_combine);
+            if (d == 0) {
+                float M = m_w[0][h];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
+                splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2], M, a.fuse_combine);
+                splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2 + 1], l, a.fuse_combine);
+            }
         }
-        for (int h = threadIdx.x; h < R; h += kThreads) {
-            a.part_ml[((head0 + h) * S + split) * 2] = M_s[h];
-            a.part_ml[((head0 + h) * S + split) * 2 + 1] = l_s[h];
-        }
+    }
+    if (S > 1 && a.fuse_combine) {
+        const int n_active = active_splits(L, a.split_len, S);
+        if (splitkv_arrive(a.counters + bg, n_active))
+            splitkv_merge_bf16(a, head0, R, n_active, static_cast<uint16_t *>(a.out));
     }
 }
 

@@ -7,24 +7,31 @@
 // section "Grouped-query attention (GQA)"; group of head h is h / (H/G), "LLM principles --
 // code implementation of multi-head attention (MQA and GQA)", section 5].
 //
-// Work: one single-wave workgroup per (sequence b, KV head g, key range), so there is no
-// barrier anywhere. The wave streams 32-row tiles of K and V with 16-byte loads: lane l
-// reads 8 head dims (chunk l%16) of row 4*i + l/16, i = 0..7, so one instruction covers
-// four whole 256-byte rows. Each lane forms the partial dot products of its 8 dims with the
-// R query rows and a DPP reduction over the 16 lanes of the row completes them (no LDS
-// traffic). The four row groups keep separate online-softmax states (running max, running
-// sum, 8-dim accumulators per head), updated once per tile, and merge at the end with four
-// cross-row exchanges. The first tile is requested before the sequence length is known, so
-// its latency overlaps the seq_lens read; rows past the end are masked by index.
+// Work: one workgroup of 4 independent waves per (sequence b, KV head g, key range); wave w
+// streams 32-row tiles w, w+4, ... of the range with 16-byte loads: lane l reads 8 head dims
+// (chunk l%16) of row 4*i + l/16, i = 0..7, so one instruction covers four whole 256-byte
+// rows. Each lane forms the partial dot products of its 8 dims with the R query rows and a
+// DPP reduction over the 16 lanes of the row completes them (no LDS traffic). Each lane
+// group keeps its own online-softmax state (running max, running sum, 8-dim accumulators
+// per head), updated once per tile; the 16 states of the workgroup are merged in one LDS
+// step at the end. Each wave's first tile is requested before the sequence length is
+// known, so its latency overlaps the seq_lens read; rows past the end are masked by index.
+// Split ranges either leave partials for the combine kernel or, when small, are merged by
+// the workgroup that finishes last (splitkv.h).
 #include "dtypes.h"
 #include "gqa_internal.h"
 #include "mfma_util.h"
+#include "splitkv.h"
 
 namespace gqa {
 
 namespace {
 
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32;  // rows per tile (8 per lane)
+constexpr int kStates = 4 * kWaves;  // softmax states per workgroup (4 row groups per wave)
+constexpr int kPassHeads = 4;        // heads merged per LDS pass
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;
 
@@ -53,8 +60,13 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 template <int RP>
-__global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(AttnArgs a) {
+    constexpr int PH = RP < kPassHeads ? RP : kPassHeads;
+    __shared__ float st_m[kStates][RP], st_l[kStates][RP];
+    __shared__ float M_s[RP], l_s[RP];
+    __shared__ __attribute__((aligned(16))) float st_acc[kStates][PH][kD];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;    // row group: rows 4*i + grp of each tile
     const int chunk = lane & 15;  // head dims 8*chunk .. 8*chunk+7
     // Split-major block order (see decode_mfma.hip).
@@ -81,19 +93,26 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
         }
     };
 
-    // First tile first: its rows are known before the length (clamped to the allocation).
-    if (kb < a.Tk) load(kb, a.Tk - 1);
+    // The query rows and the first tile do not depend on the length (the tile's rows are
+    // clamped to the allocation), so all three requests share one memory round trip.
+    i32x4_t qraw[RP];
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + head0 * kD;
+#pragma unroll
+    for (int h = 0; h < RP; ++h) qraw[h] = *(const i32x4_t *)(qp + (long)(h < R ? h : R - 1) * kD + 8 * chunk);
+    if (kb + wave * kRows < a.Tk) load(kb + wave * kRows, a.Tk - 1);
 
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
     const int ke = kb + a.split_len < L ? kb + a.split_len : L;
 
     if (kb >= ke) {
-        if (S == 1) {
+        // Nothing to attend to in this range. Fused merges count only non-empty ranges, so
+        // an empty one only has to produce the zero row of an empty sequence.
+        if (S == 1 || (a.fuse_combine && L == 0 && split == 0)) {
             uint16_t *out = static_cast<uint16_t *>(a.out);
-            for (int e = lane; e < R * kD; e += 64) out[head0 * kD + e] = 0;
-        } else {
-            for (int h = lane; h < R; h += 64) {
+            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
+        } else if (!a.fuse_combine) {
+            for (int h = threadIdx.x; h < R; h += kThreads) {
                 a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
                 a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
             }
@@ -103,12 +122,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
 
     // This lane's 8 dims of every query row of the group, pre-scaled into the base-2 domain.
     float q[RP][8];
-    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + head0 * kD;
 #pragma unroll
     for (int h = 0; h < RP; ++h) {
         if (h < R) {
-            const i32x4_t w = *(const i32x4_t *)(qp + (long)h * kD + 8 * chunk);
-            bf16x8_to_f32(w, q[h]);
+            bf16x8_to_f32(qraw[h], q[h]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) q[h][e] *= a.scale_log2;
         } else {
@@ -126,7 +143,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
-    for (int t0 = kb; t0 < ke; t0 += kRows) {
+    for (int t0 = kb + wave * kRows; t0 < ke; t0 += kWaves * kRows) {
         i32x4_t kc[8], vc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -135,7 +152,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
         }
         // Unconditional, branch-free prefetch of the next tile (past the end it re-reads this
         // tile from cache), pinned ahead of this tile's work.
-        load(t0 + kRows < ke ? t0 + kRows : t0, ke - 1);
+        load(t0 + kWaves * kRows < ke ? t0 + kWaves * kRows : t0, ke - 1);
         __builtin_amdgcn_sched_barrier(0);
 
         // Rows at or past the end (the last tile, or a first tile loaded before the length
@@ -194,60 +211,67 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(AttnArgs a) {
         }
     }
 
-    // ---- merge the four row-group states (lanes chunk, chunk+16, +32, +48), fixed order ----
+    // ---- merge the 16 states of the workgroup (fixed order: deterministic) ----
+    const int sid = wave * 4 + grp;
+    if (chunk == 0) {
 #pragma unroll
-    for (int h = 0; h < RP; ++h) {
-        float M = fmaxf(m[h], __shfl_xor(m[h], 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = m[h] == -INFINITY ? 0.f : fast_exp2(m[h] - M);
-        float l = lsum[h] * f;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[h][e] * f;
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            acc[h][e] = x;
+        for (int h = 0; h < RP; ++h) {
+            st_m[sid][h] = m[h];
+            st_l[sid][h] = lsum[h];
         }
-        m[h] = M;
-        lsum[h] = l;
     }
-
-    if (grp == 0) {
-        if (S == 1) {
-            uint16_t *out = static_cast<uint16_t *>(a.out);
+    __syncthreads();
+    if (threadIdx.x < RP) {
+        const int h = threadIdx.x;
+        float M = st_m[0][h];
+        for (int i = 1; i < kStates; ++i) M = fmaxf(M, st_m[i][h]);
+        float l = 0.f;
+        for (int i = 0; i < kStates; ++i) l += st_m[i][h] == -INFINITY ? 0.f : fast_exp2(st_m[i][h] - M) * st_l[i][h];
+        M_s[h] = M;
+        l_s[h] = l;
+    }
+    __syncthreads();
+    uint16_t *out = static_cast<uint16_t *>(a.out);
 #pragma unroll
-            for (int h = 0; h < RP; ++h) {
-                if (h < R) {
-                    const float inv = 1.f / lsum[h];
-                    i32x4_t w;
+    for (int h0 = 0; h0 < RP; h0 += PH) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = pack_bf16_rne(acc[h][2 * e] * inv, acc[h][2 * e + 1] * inv);
-                    *(i32x4_t *)(out + (head0 + h) * kD + 8 * chunk) = w;
-                }
-            }
-        } else {
+        for (int hh = 0; hh < PH; ++hh) {
+            const float f = m[h0 + hh] == -INFINITY ? 0.f : fast_exp2(m[h0 + hh] - M_s[h0 + hh]);
+            *(f32x4_t *)&st_acc[sid][hh][8 * chunk] =
+                f32x4_t{acc[h0 + hh][0] * f, acc[h0 + hh][1] * f, acc[h0 + hh][2] * f, acc[h0 + hh][3] * f};
+            *(f32x4_t *)&st_acc[sid][hh][8 * chunk + 4] =
+                f32x4_t{acc[h0 + hh][4] * f, acc[h0 + hh][5] * f, acc[h0 + hh][6] * f, acc[h0 + hh][7] * f};
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < PH * kD; e += kThreads) {
+            const int hh = e / kD, d = e % kD, h = h0 + hh;
+            if (h < R) {
+                float x = 0.f;
 #pragma unroll
-            for (int h = 0; h < RP; ++h) {
-                if (h < R) {
-                    float *pa = a.part_acc + ((head0 + h) * S + split) * kD + 8 * chunk;
-                    *(f32x4_t *)pa = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-                    *(f32x4_t *)(pa + 4) = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-                    if (chunk == 0) {
-                        a.part_ml[((head0 + h) * S + split) * 2] = m[h];
-                        a.part_ml[((head0 + h) * S + split) * 2 + 1] = lsum[h];
-                    }
-                }
+                for (int i = 0; i < kStates; ++i) x += st_acc[i][hh][d];
+                if (S == 1)
+                    out[(head0 + h) * kD + d] = f32_to_bf16(x / l_s[h]);
+                else
+                    splitkv_store(&a.part_acc[((head0 + h) * S + split) * kD + d], x, a.fuse_combine);
             }
         }
+        __syncthreads();
+    }
+    if (S == 1) return;
+    for (int h = threadIdx.x; h < R; h += kThreads) {
+        splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2], M_s[h], a.fuse_combine);
+        splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2 + 1], l_s[h], a.fuse_combine);
+    }
+    if (a.fuse_combine) {
+        const int n_active = active_splits(L, a.split_len, S);
+        if (splitkv_arrive(a.counters + bg, n_active)) splitkv_merge_bf16(a, head0, R, n_active, out);
     }
 }
 
 template <int RP>
 hipError_t launch_rp(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_valu_kernel<RP>), dim3((unsigned)(a.B * a.G * a.num_splits)), dim3(64), 0, stream,
-                       a);
+    hipLaunchKernelGGL((decode_valu_kernel<RP>), dim3((unsigned)(a.B * a.G * a.num_splits)), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

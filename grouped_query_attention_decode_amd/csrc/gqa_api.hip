@@ -71,12 +71,26 @@ int resolve_splits(int B, int H, int G, int D, int T_cap, int kv_dtype, int requ
     return s;
 }
 
-size_t workspace_bytes_for(long B, long H, long D, long S) {
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return ((x + kAlign - 1) / kAlign) * kAlign; }
+
+// Workspace layout: [B*G] int arrival counters | [B*H][S][D] fp32 partial accumulators |
+// [B*H][S][2] fp32 (running max, running sum); each part 256-byte aligned.
+size_t counter_bytes(long B, long G) { return round_up((size_t)B * G * sizeof(int)); }
+size_t acc_bytes(long B, long H, long D, long S) { return round_up((size_t)B * H * S * D * sizeof(float)); }
+
+size_t workspace_bytes_for(long B, long H, long G, long D, long S) {
     if (S <= 1) return 0;
-    const size_t acc = (size_t)B * H * S * D * sizeof(float);
-    const size_t ml = (size_t)B * H * S * 2 * sizeof(float);
-    const size_t align = 256;
-    return ((acc + align - 1) / align) * align + ml;
+    return counter_bytes(B, G) + acc_bytes(B, H, D, S) + (size_t)B * H * S * 2 * sizeof(float);
+}
+
+// The workgroup that finishes a group's last key range merges the partials itself when
+// they are small enough for one workgroup to read quickly; otherwise a combine kernel
+// spreads the merge over B*H workgroups.
+constexpr size_t kFuseMaxBytes = 64 * 1024;
+bool fuse_combine_for(long H, long G, long D, long S) {
+    // The in-kernel merge keeps one weight per (head, range) in a 128-entry LDS table.
+    return S > 1 && S * (H / G) <= 128 && (size_t)S * (H / G) * (D + 2) * sizeof(float) <= kFuseMaxBytes;
 }
 
 // gfx950 check, once per device.
@@ -132,7 +146,7 @@ int gqa_decode_num_splits(int B, int H, int G, int D, int kv_capacity, int kv_dt
 size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, int kv_dtype, int num_splits) {
     const int S = gqa_decode_num_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
     if (S == 0) return SIZE_MAX;
-    return workspace_bytes_for(B, H, D, S);
+    return workspace_bytes_for(B, H, G, D, S);
 }
 
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
@@ -177,7 +191,7 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     if (path == GQA_PATH_VALU && !decode_valu_supports(a)) return GQA_ERR_UNSUPPORTED;
     if (path == GQA_PATH_MFMA && !decode_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
 
-    const size_t need = workspace_bytes_for(B, H, D, a.num_splits);
+    const size_t need = workspace_bytes_for(B, H, G, D, a.num_splits);
     if (need > 0 && o.workspace && o.workspace_bytes < need) return GQA_ERR_WORKSPACE;
     if (need > 0 && o.workspace && ((uintptr_t)o.workspace % 16) != 0) return GQA_ERR_INVALID_ARG;
 
@@ -190,18 +204,25 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     if (need > 0 && !ws) {
         if (hipMallocAsync(&ws, need, stream) != hipSuccess) return GQA_ERR_HIP;
         owned = true;
+        // Fresh memory: the arrival counters must start at zero.
+        if (hipMemsetAsync(ws, 0, counter_bytes(B, G), stream) != hipSuccess) {
+            (void)hipFreeAsync(ws, stream);
+            return GQA_ERR_HIP;
+        }
     }
     if (need > 0) {
-        const size_t acc_bytes = (size_t)B * H * a.num_splits * D * sizeof(float);
-        a.part_acc = static_cast<float *>(ws);
-        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((acc_bytes + 255) / 256) * 256);
+        char *base = static_cast<char *>(ws);
+        a.counters = reinterpret_cast<int *>(base);
+        a.part_acc = reinterpret_cast<float *>(base + counter_bytes(B, G));
+        a.part_ml = reinterpret_cast<float *>(base + counter_bytes(B, G) + acc_bytes(B, H, D, a.num_splits));
+        a.fuse_combine = path != GQA_PATH_GENERIC && fuse_combine_for(H, G, D, a.num_splits);
     }
 
     hipError_t e;
     if (path == GQA_PATH_MFMA) e = launch_decode_mfma(a, stream);
     else if (path == GQA_PATH_VALU) e = launch_decode_valu(a, stream);
     else e = launch_generic(a, stream);
-    if (e == hipSuccess && a.num_splits > 1) e = launch_combine(a, stream);
+    if (e == hipSuccess && a.num_splits > 1 && !a.fuse_combine) e = launch_combine(a, stream);
     if (owned) {
         const hipError_t f = hipFreeAsync(ws, stream);
         if (e == hipSuccess) e = f;

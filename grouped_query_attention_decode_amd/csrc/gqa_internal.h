@@ -19,6 +19,8 @@ struct AttnArgs {
     const float *v_scale;
     float *part_acc;          // split partials, [B*H][S][D] (unnormalised)
     float *part_ml;           // split partials, [B*H][S][2] = (running max, running sum)
+    int *counters;            // split arrival counters, [B*G], zero between calls
+    int fuse_combine;         // 1: the last workgroup of each (b, g) merges the partials
     int B, H, G, D;
     int Tq;                   // query rows per (b, h): 1 for decode, T for prefill
     int Tk;                   // key rows allocated per (b, g): T_cap or T

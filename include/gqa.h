@@ -114,7 +114,10 @@ void gqa_opts_init(gqa_opts *opts);
  * by a log-sum-exp combine ["GQA revolution ...", section on split-KV block
  * computation]; that needs device scratch: opts->workspace of at least
  * gqa_decode_workspace_size() bytes, or NULL to let the call take stream-ordered
- * memory with hipMallocAsync/hipFreeAsync on `stream`.
+ * memory with hipMallocAsync/hipFreeAsync on `stream`. A caller workspace must be
+ * zero-filled before its first use (it holds per-(sequence, KV head) arrival counters);
+ * every completed call leaves it ready for the next one. Calls that run concurrently must
+ * not share a workspace.
  *
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
  * opts is required (it carries kv_capacity). D in 1..256.

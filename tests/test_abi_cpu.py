@@ -129,8 +129,10 @@ def test_split_queries(lib):
     assert gqa.decode_num_splits(2, 8, 2, 64, 10, "bf16", 7) == 7
     assert gqa.decode_num_splits(2, 8, 2, 64, 10, "bf16", 64) == 64
     S = 5
-    acc = 2 * 8 * S * 64 * 4
-    assert gqa.decode_workspace_size(2, 8, 2, 64, 100, "bf16", S) == ((acc + 255) // 256) * 256 + 2 * 8 * S * 2 * 4
+    up = lambda x: ((x + 255) // 256) * 256
+    counters = up(2 * 2 * 4)            # one int per (sequence, KV head)
+    acc = up(2 * 8 * S * 64 * 4)        # [B*H][S][D] fp32
+    assert gqa.decode_workspace_size(2, 8, 2, 64, 100, "bf16", S) == counters + acc + 2 * 8 * S * 2 * 4
     # automatic choice: between 1 and the number of keys, deterministic
     for args in [(1, 32, 8, 128, 2048, "bf16"), (16, 64, 8, 128, 4096, "bf16"), (8, 32, 1, 128, 32768, "fp8_e4m3fn"),
                  (1, 4, 2, 3, 7, "f32")]:
