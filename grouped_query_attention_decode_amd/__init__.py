@@ -18,13 +18,14 @@ import os
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
 __all__ = ["decode", "prefill", "decode_num_splits", "decode_workspace_size", "status_string",
-           "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES"]
+           "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
 
 GQA_OK = 0
 DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3fn": 2}
 PATHS = {"auto": 0, "generic": 1, "valu": 2, "mfma": 3}
+LAYOUTS = {"auto": 0, "uniform": 1, "flat": 2}
 _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
 
 
@@ -44,7 +45,7 @@ class GqaOpts(ctypes.Structure):
         ("kv_capacity", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("path", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
@@ -142,8 +143,11 @@ def _stream_handle(stream, device) -> int:
 
 
 def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
-           num_splits=0, path="auto", workspace=None, stream=None):
+           num_splits=0, path="auto", workspace=None, stream=None, layout="auto"):
     """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype).
+
+    ``layout`` ("auto", "uniform" or "flat") chooses how the key rows are spread over the
+    workgroups; "flat" balances batches of unequal lengths (matrix-core path only).
 
     ``workspace`` (uint8 device tensor of at least ``decode_workspace_size`` bytes) must be
     zero-filled before its first use; each completed call leaves it ready for the next.
@@ -165,7 +169,7 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
         scale = 1.0 / math.sqrt(D)
     kv_code = _dtype_code(k_cache, "k_cache")
     o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
-                 num_splits=int(num_splits), path=PATHS[path])
+                 num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
     if kv_code == DTYPES["fp8_e4m3fn"]:
         if k_scale is None or v_scale is None:
             raise ValueError("fp8 caches need k_scale and v_scale")

@@ -89,34 +89,10 @@ __device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, cons
     }
 }
 
+// Q^T as the B operand: lane l holds Q[head 16*hb + l%16][dk .. dk+7] for k-step kk. Padded
+// heads (index >= R) load head R-1 so that the loads stay unconditional; attend() zeroes them.
 template <int NHB, bool FP8>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
-    constexpr int RB = FP8 ? 128 : 256;
-    constexpr int VT = kBlockT * RB;                     // V tile bytes per wave
-    constexpr int HP = 16 * NHB;                         // heads padded to MFMA blocks
-    constexpr int EPI = kWaves * HP * kD * 4;            // per-wave accumulator slices
-    constexpr int LDS_BYTES = kWaves * VT > EPI ? kWaves * VT : EPI;
-    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-    __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    // Split-major order: the blocks resident on one CU at once are far apart in the grid and
-    // so pair long (early) key ranges with short or empty (late) ones of ragged batches.
-    const int S = a.num_splits;
-    const int nbg = a.B * a.G;
-    const int split = blockIdx.x / nbg;
-    const int bg = blockIdx.x % nbg;
-    const int G = a.G, H = a.H, R = H / G;
-    const int b = bg / G, g = bg % G;
-    const int kb = split * a.split_len;
-    const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
-
-    // Q^T as the B operand: lane l holds Q[head 16*hb + l%16][32*kk + 8*(l/16) .. +7]. The query,
-    // the scales and this wave's first block do not depend on the length (the block's rows are
-    // clamped to the allocation), so they are requested before it and share its round trip.
-    i32x4_t qT[NHB][4];
-    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + head0 * kD;
+__device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp, int R, int lane) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         const int h = hb * 16 + (lane & 15);
@@ -128,39 +104,32 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
             qT[hb][kk] = *(const i32x4_t *)(qp + (long)(h < R ? h : R - 1) * kD + dk);
         }
     }
-    const float kscale = FP8 ? a.k_scale[bg] : 1.f;
-    const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+}
 
-    const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
-    const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
-    int t0 = kb + wave * kBlockT;
-    Frag<FP8> nxt;
-    if (t0 < a.Tk) load_block<FP8>(nxt, kbase, vbase, t0, a.Tk, lane);
+// Where one call of attend() leaves its result.
+struct PieceOut {
+    int slot;     // partial slot of this key range
+    int n_slots;  // key ranges of this (sequence, KV head) that hold keys
+    bool direct;  // the range covers the whole sequence: write the output itself
+};
 
-    int L = a.seq_lens[b];
-    L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
-    const int ke = kb + a.split_len < L ? kb + a.split_len : L;
-
-    if (kb >= ke) {  // nothing to attend to in this range
-        // Fused merges count only non-empty ranges, so an empty one only has to produce the
-        // zero row of an empty sequence.
-        if (S == 1 || (a.fuse_combine && L == 0 && split == 0)) {
-            uint16_t *out = static_cast<uint16_t *>(a.out);
-            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
-        } else if (!a.fuse_combine) {
-            for (int h = threadIdx.x; h < R; h += kThreads) {
-                a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
-                a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
-            }
-        }
-        return;
-    }
+// Attention of query heads head0 .. head0+R-1 over key rows kb .. ke-1 of one (sequence, KV
+// head), by the whole workgroup: each wave streams blocks kb + 32 (wave + 4 i), then the four
+// waves merge. The caller has requested q (qT) and this wave's first block (nxt) already.
+template <int NHB, bool FP8>
+__device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w)[16 * NHB], float (*l_w)[16 * NHB],
+                                       int lane, int wave, long head0, int R, int bg, int kb, int ke, PieceOut po,
+                                       i32x4_t (&qT)[NHB][4], Frag<FP8> &nxt, const char *kbase,
+                                       const char *vbase, float c, float vscale) {
+    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int VT = kBlockT * RB;  // V tile bytes per wave
+    constexpr int HP = 16 * NHB;      // heads padded to MFMA blocks
+    const int S = a.num_splits;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
         if (hb * 16 + (lane & 15) >= R)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qT[hb][kk] = i32x4_t{0, 0, 0, 0};
-    const float c = a.scale_log2 * kscale;
     char *vt = lds + wave * VT;
 
     f32x4_t o[NHB][8];
@@ -173,11 +142,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
         for (int nb = 0; nb < 8; ++nb) o[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (; t0 < ke; t0 += kWaves * kBlockT) {
-        Frag<FP8> cur = nxt;
-        // Only a first block (requested before the length was known) can hold rows at or past
-        // the end; they may contain anything, NaN included. Their scores are masked by index
-        // below; zero their values so that the zero probabilities stay exact.
+    // One 32-token block: `slot` holds its K/V rows (requested earlier) and is refilled with
+    // the block `dist` rows ahead.
+    auto step = [&](Frag<FP8> &slot, int t0, int dist) {
+        Frag<FP8> cur = slot;
+        // Rows at or past the end may hold anything, NaN included (a first block requested
+        // before the length was known reads up to the allocation). Their scores are masked by
+        // index below; zero their values so that the zero probabilities stay exact.
         if (t0 + kBlockT > ke) {
             if constexpr (FP8) {
 #pragma unroll
@@ -204,12 +175,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
                 *(i32x4_t *)(vt + r * RB + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
             }
         }
-        // Prefetch the next block before this block's work. The load is unconditional and
+        // Prefetch this slot's next block (dist rows ahead) before this block's work. The load is unconditional and
         // branch-free (past the end it re-reads the current block, which the cache holds),
         // and the barrier keeps the scheduler from sinking it next to its use -- otherwise
         // every block waits out a full memory latency.
-        const int tn = t0 + kWaves * kBlockT < ke ? t0 + kWaves * kBlockT : t0;
-        load_block<FP8>(nxt, kbase, vbase, tn, ke, lane);
+        const int tn = t0 + dist < ke ? t0 + dist : t0;
+        load_block<FP8>(slot, kbase, vbase, tn, ke, lane);
         __builtin_amdgcn_sched_barrier(0);
 
         // S^T = K . Q^T for both 16-token sub-blocks and every head block.
@@ -297,7 +268,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) o[hb][nb] = mfma16x16x32(va, pb[hb], o[hb][nb]);
         }
-    }
+        };
+    constexpr int kStep = kWaves * kBlockT;
+    for (int t0 = kb + wave * kBlockT; t0 < ke; t0 += kStep) step(nxt, t0, kStep);
 
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
     // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
@@ -342,34 +315,190 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
             acc[3] += x[3];
             l += l_w[w][h];
         }
-        if (S == 1) {
+        if (po.direct) {
             const float inv = vscale / l;
             uint16_t *out = static_cast<uint16_t *>(a.out) + (head0 + h) * kD + d;
             *(i32x2_t *)out = i32x2_t{pack_bf16_rne(acc[0] * inv, acc[1] * inv), pack_bf16_rne(acc[2] * inv, acc[3] * inv)};
         } else {
-            float *pa = &a.part_acc[((head0 + h) * S + split) * kD + d];
+            float *pa = &a.part_acc[((head0 + h) * S + po.slot) * kD + d];
             splitkv_store4(pa, f32x4_t{acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale},
                            a.fuse_combine);
             if (d == 0) {
                 float M = m_w[0][h];
 #pragma unroll
                 for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
-                splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2], M, a.fuse_combine);
-                splitkv_store(&a.part_ml[((head0 + h) * S + split) * 2 + 1], l, a.fuse_combine);
+                splitkv_store(&a.part_ml[((head0 + h) * S + po.slot) * 2], M, a.fuse_combine);
+                splitkv_store(&a.part_ml[((head0 + h) * S + po.slot) * 2 + 1], l, a.fuse_combine);
             }
         }
     }
-    if (S > 1 && a.fuse_combine) {
-        const int n_active = active_splits(L, a.split_len, S);
-        if (splitkv_arrive(a.counters + bg, n_active))
-            splitkv_merge_bf16(a, head0, R, n_active, static_cast<uint16_t *>(a.out));
+    if (!po.direct && a.fuse_combine) {
+        if (splitkv_arrive(a.counters + bg, po.n_slots))
+            splitkv_merge_bf16(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
+    }
+}
+
+// Uniform layout: workgroup = (key range `split`, sequence b, KV head g), ranges of split_len
+// keys. Split-major order: the blocks resident on one CU at once are far apart in the grid.
+template <int NHB, bool FP8>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
+    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int HP = 16 * NHB;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kD * 4 ? kWaves * kBlockT * RB : kWaves * HP * kD * 4;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
+    const int S = a.num_splits;
+    const int nbg = a.B * a.G;
+    const int split = blockIdx.x / nbg;
+    const int bg = blockIdx.x % nbg;
+    const int G = a.G, H = a.H, R = H / G;
+    const int b = bg / G, g = bg % G;
+    const int kb = split * a.split_len;
+    const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
+
+    // The query, the scales and this wave's first block do not depend on the length (the
+    // block's rows are clamped to the allocation), so they are requested before it and share
+    // its round trip.
+    i32x4_t qT[NHB][4];
+    load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
+    const float kscale = FP8 ? a.k_scale[bg] : 1.f;
+    const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+    const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
+    const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+    Frag<FP8> nxt;
+    if (kb + wave * kBlockT < a.Tk) load_block<FP8>(nxt, kbase, vbase, kb + wave * kBlockT, a.Tk, lane);
+
+    const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Tk));
+    const int ke = kb + a.split_len < L ? kb + a.split_len : L;
+
+    if (kb >= ke) {  // nothing to attend to in this range
+        // Fused merges count only non-empty ranges, so an empty one only has to produce the
+        // zero row of an empty sequence.
+        if (S == 1 || (a.fuse_combine && L == 0 && split == 0)) {
+            uint16_t *out = static_cast<uint16_t *>(a.out);
+            for (int e = threadIdx.x; e < R * kD; e += kThreads) out[head0 * kD + e] = 0;
+        } else if (!a.fuse_combine) {
+            for (int h = threadIdx.x; h < R; h += kThreads) {
+                a.part_ml[((head0 + h) * S + split) * 2] = -INFINITY;
+                a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
+            }
+        }
+        return;
+    }
+    PieceOut po;
+    po.slot = split;
+    po.n_slots = active_splits(L, a.split_len, S);
+    // With the in-kernel merge, a sequence whose keys all fall in this range needs no merge.
+    po.direct = S == 1 || (a.fuse_combine && po.n_slots == 1);
+    attend<NHB, FP8>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, kbase, vbase,
+                     a.scale_log2 * kscale, vscale);
+}
+
+// Flat layout (splitkv.h): workgroup w streams rows [w C, (w + 1) C) of the concatenated
+// segments, piece by piece. Every workgroup gets the same number of rows, whatever the mix of
+// sequence lengths.
+template <int NHB, bool FP8>
+__global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_kernel(AttnArgs a) {
+    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int HP = 16 * NHB;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kD * 4 ? kWaves * kBlockT * RB : kWaves * HP * kD * 4;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
+    __shared__ int lay_s[4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
+    const int G = a.G, H = a.H, R = H / G, B = a.B;
+
+    // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row.
+    if (wave == 0) {
+        const int Ng = flat_total(a.seq_lens, B, a.Tk, lane);
+        const int C = flat_chunk(G * Ng, gridDim.x, a.flat_cmin);
+        const int x0 = (int)blockIdx.x * C;
+        int b0 = 0, p0 = 0, g0 = 0;
+        if (x0 < G * Ng) {
+            g0 = x0 / Ng;
+            flat_find(a.seq_lens, B, a.Tk, x0 - g0 * Ng, lane, b0, p0);
+        }
+        if (lane == 0) {
+            lay_s[0] = Ng;
+            lay_s[1] = C;
+            lay_s[2] = g0 * B + b0;
+            lay_s[3] = p0;
+        }
+    }
+    __syncthreads();
+    // Workgroup-uniform from here on: scalar registers, scalar branches.
+    const int Ng = __builtin_amdgcn_readfirstlane(lay_s[0]);
+    const int C = __builtin_amdgcn_readfirstlane(lay_s[1]);
+    const int gb0 = __builtin_amdgcn_readfirstlane(lay_s[2]);
+    int Pb = __builtin_amdgcn_readfirstlane(lay_s[3]);
+    const int N = G * Ng;
+
+    if (blockIdx.x == 0 && a.fuse_combine) {
+        // Sequences without keys belong to no piece: their output rows are zero.
+        uint16_t *out = static_cast<uint16_t *>(a.out);
+        for (int k0 = 0; k0 < B; k0 += 64) {
+            const int bb = k0 + lane;
+            unsigned long long empty = __ballot(bb < B && clamp_len(a.seq_lens[bb], a.Tk) == 0);
+            while (empty) {
+                const int be = k0 + __ffsll((long long)empty) - 1;
+                empty &= empty - 1;
+                for (int e = threadIdx.x; e < H * kD; e += kThreads) out[(long)be * H * kD + e] = 0;
+            }
+        }
+    }
+
+    int x = (int)blockIdx.x * C;
+    const int xe = x + C < N ? x + C : N;
+    int g = gb0 / B, b = gb0 % B;
+    while (x < xe) {
+        const int Tb = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Tk));
+        const int s0 = g * Ng + Pb;  // first row of segment (b, g)
+        if (x >= s0 + Tb) {          // segment done (or empty): next one
+            Pb += Tb;
+            if (++b == B) {
+                b = 0;
+                Pb = 0;
+                ++g;
+            }
+            continue;
+        }
+        const int kb = x - s0;
+        const int ke = xe - s0 < Tb ? xe - s0 : Tb;
+        const int bg = b * G + g;
+        const long head0 = (long)b * H + (long)g * R;
+        PieceOut po;
+        po.n_slots = flat_pieces(Ng, C, Pb, Tb, g);
+        po.slot = (int)blockIdx.x - (int)((unsigned)s0 / (unsigned)C);
+        po.direct = po.n_slots == 1;
+
+        i32x4_t qT[NHB][4];
+        load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
+        const float kscale = FP8 ? a.k_scale[bg] : 1.f;
+        const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+        const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
+        const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+        Frag<FP8> nxt;
+        if (kb + wave * kBlockT < ke) load_block<FP8>(nxt, kbase, vbase, kb + wave * kBlockT, ke, lane);
+        attend<NHB, FP8>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, kbase, vbase,
+                         a.scale_log2 * kscale, vscale);
+        __syncthreads();  // the next piece reuses the LDS tiles
+        x = s0 + ke;
     }
 }
 
 template <int NHB, bool FP8>
 hipError_t launch_nhb(const AttnArgs &a, hipStream_t stream) {
-    dim3 grid((unsigned)(a.B * a.G * a.num_splits));
-    hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8>), grid, dim3(kThreads), 0, stream, a);
+    if (a.flat) {
+        hipLaunchKernelGGL((decode_mfma_flat_kernel<NHB, FP8>), dim3((unsigned)a.flat_nw), dim3(kThreads), 0, stream, a);
+    } else {
+        dim3 grid((unsigned)(a.B * a.G * a.num_splits));
+        hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(AttnArgs a) {
     __shared__ float M_s[RP], l_s[RP];
     __shared__ __attribute__((aligned(16))) float st_acc[kStates][PH][kD];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
     const int grp = lane >> 4;    // row group: rows 4*i + grp of each tile
     const int chunk = lane & 15;  // head dims 8*chunk .. 8*chunk+7
     // Split-major block order (see decode_mfma.hip).

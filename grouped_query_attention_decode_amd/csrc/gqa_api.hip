@@ -71,6 +71,84 @@ int resolve_splits(int B, int H, int G, int D, int T_cap, int kv_dtype, int requ
     return s;
 }
 
+// Partial results of one key range merged inside the decode kernel up to this size.
+constexpr size_t kFuseMaxBytes = 64 * 1024;
+bool fuse_combine_for(long H, long G, long D, long S) {
+    // The in-kernel merge keeps one weight per (head, range) in a 128-entry LDS table.
+    return S > 1 && S * (H / G) <= 128 && (size_t)S * (H / G) * (D + 2) * sizeof(float) <= kFuseMaxBytes;
+}
+
+// Decode work layout. The flat layout (equal rows per workgroup whatever the lengths) serves
+// the matrix-core family when asked for, or by default for batches of at least
+// kFlatMinBatch sequences, where lengths usually differ; its fixed cost (every workgroup
+// first reads all lengths) does not pay off for a few sequences. Otherwise uniform key ranges.
+struct DecodePlan {
+    int flat = 0;
+    int S = 1;          // key ranges (uniform) or partial slots per head (flat)
+    int split_len = 0;  // uniform
+    int nw = 0;         // flat: workgroups
+    int cmin = 0;       // flat: fewest rows per workgroup
+    int fuse = 0;       // merge inside the decode kernel
+};
+
+constexpr int kNominalCUs = 256;
+constexpr int kFlatMinBatch = 16;
+
+bool flat_possible(int B, int G, int T_cap, int path, int requested) {
+    return path == GQA_PATH_MFMA && requested == 0 && (long)B * G * T_cap < (1L << 31);
+}
+
+// `path` is the resolved kernel family (not AUTO); `layout` a gqa_layout the caller checked.
+DecodePlan plan_decode(int B, int H, int G, int D, int T_cap, int kv_dtype, int requested, int path, int layout) {
+    DecodePlan p;
+    const long R = H / G;
+    const bool mfma_path = path == GQA_PATH_MFMA;
+    const bool flat = flat_possible(B, G, T_cap, path, requested) &&
+                      (layout == GQA_LAYOUT_FLAT || (layout == GQA_LAYOUT_AUTO && B >= kFlatMinBatch));
+    if (flat) {
+        p.flat = 1;
+        // One workgroup per CU: each streams a long run of rows, so the per-piece fixed costs
+        // (lengths, first block, merge) stay small against it.
+        p.nw = kNominalCUs;
+        const long per_slot = R * (D + 2) * (long)sizeof(float);
+        const long fuse_slots = (long)kFuseMaxBytes / per_slot;
+        const long full_chunk = ((long)B * G * T_cap + p.nw - 1) / p.nw;  // rows per workgroup, full caches
+        long cmin = 256;
+        if (fuse_slots >= 3 && fuse_slots * R <= 128) {
+            // Fuse when a chunk long enough to bound the slots by fuse_slots still spreads a full
+            // batch over every workgroup.
+            const long need = ((T_cap + fuse_slots - 2) / (fuse_slots - 1) + 31) / 32 * 32;
+            if (need <= full_chunk) {
+                cmin = need > 128 ? need : 128;
+                p.fuse = 1;
+            }
+        }
+        p.cmin = (int)cmin;
+        // A segment of T rows meets at most ceil((T - 1) / C) + 1 chunks of C >= cmin rows.
+        p.S = (int)((T_cap - 1 + cmin - 1) / cmin + 1);
+        if (p.fuse && !fuse_combine_for(H, G, D, p.S)) p.fuse = 0;
+        return p;
+    }
+    p.S = resolve_splits(B, H, G, D, T_cap, kv_dtype, requested);
+    if (requested == 0 && mfma_path && !fuse_combine_for(H, G, D, p.S)) {
+        // Prefer a split count whose partials merge inside the kernel (no second kernel), if
+        // halving reaches one while at least 128 workgroups remain.
+        int s = p.S;
+        while (s > 1 && !fuse_combine_for(H, G, D, s) && (long)B * G * (s / 2) >= 128) s /= 2;
+        if (s > 1 && fuse_combine_for(H, G, D, s)) p.S = s;
+    }
+    p.split_len = (T_cap + p.S - 1) / p.S;
+    p.fuse = path != GQA_PATH_GENERIC && fuse_combine_for(H, G, D, p.S);
+    return p;
+}
+
+// AUTO resolves to the matrix-core family wherever it applies: head dim 128 with a bf16 or fp8
+// cache (the cache type fixes q's: bf16), at most 64 query heads per KV head.
+int auto_path(int H, int G, int D, int kv_dtype) {
+    if (D == 128 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && H / G <= 64) return GQA_PATH_MFMA;
+    return GQA_PATH_GENERIC;
+}
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return ((x + kAlign - 1) / kAlign) * kAlign; }
 
@@ -84,14 +162,6 @@ size_t workspace_bytes_for(long B, long H, long G, long D, long S) {
     return counter_bytes(B, G) + acc_bytes(B, H, D, S) + (size_t)B * H * S * 2 * sizeof(float);
 }
 
-// The workgroup that finishes a group's last key range merges the partials itself when
-// they are small enough for one workgroup to read quickly; otherwise a combine kernel
-// spreads the merge over B*H workgroups.
-constexpr size_t kFuseMaxBytes = 64 * 1024;
-bool fuse_combine_for(long H, long G, long D, long S) {
-    // The in-kernel merge keeps one weight per (head, range) in a 128-entry LDS table.
-    return S > 1 && S * (H / G) <= 128 && (size_t)S * (H / G) * (D + 2) * sizeof(float) <= kFuseMaxBytes;
-}
 
 // gfx950 check, once per device.
 std::mutex g_arch_mu;
@@ -140,12 +210,22 @@ const char *gqa_status_string(gqa_status s) {
 int gqa_decode_num_splits(int B, int H, int G, int D, int kv_capacity, int kv_dtype, int num_splits) {
     if (!decode_sizes_ok(B, H, G, D, kv_capacity) || !valid_dtype(kv_dtype)) return 0;
     if (num_splits < 0 || num_splits > kMaxSplitsAbi) return 0;
-    return resolve_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
+    return plan_decode(B, H, G, D, kv_capacity, kv_dtype, num_splits, auto_path(H, G, D, kv_dtype), GQA_LAYOUT_AUTO)
+        .S;
 }
 
 size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, int kv_dtype, int num_splits) {
-    const int S = gqa_decode_num_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
+    int S = gqa_decode_num_splits(B, H, G, D, kv_capacity, kv_dtype, num_splits);
     if (S == 0) return SIZE_MAX;
+    // Enough for every kernel family and layout a caller may force as well.
+    const int path = auto_path(H, G, D, kv_dtype);
+    for (int layout : {GQA_LAYOUT_UNIFORM, GQA_LAYOUT_FLAT}) {
+        const int s = plan_decode(B, H, G, D, kv_capacity, kv_dtype, num_splits, path, layout).S;
+        if (s > S) S = s;
+    }
+    const int s_generic = plan_decode(B, H, G, D, kv_capacity, kv_dtype, num_splits, GQA_PATH_GENERIC,
+                                      GQA_LAYOUT_UNIFORM).S;
+    if (s_generic > S) S = s_generic;
     return workspace_bytes_for(B, H, G, D, S);
 }
 
@@ -156,7 +236,8 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
     gqa_opts o;
     if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
-    if (o.reserved0 != 0) return GQA_ERR_INVALID_ARG;
+    if (o.layout < GQA_LAYOUT_AUTO || o.layout > GQA_LAYOUT_FLAT) return GQA_ERR_INVALID_ARG;
+    if (o.layout == GQA_LAYOUT_FLAT && o.num_splits > 0) return GQA_ERR_INVALID_ARG;
     if (!decode_sizes_ok(B, H, G, D, o.kv_capacity)) return GQA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
     if (o.num_splits < 0 || o.num_splits > kMaxSplitsAbi) return GQA_ERR_INVALID_ARG;
@@ -178,18 +259,19 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     a.causal = 0; a.decode = 1;
     a.scale_log2 = scale * kLog2e;
     a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
-    a.num_splits = resolve_splits(B, H, G, D, o.kv_capacity, o.kv_dtype, o.num_splits);
-    a.split_len = (o.kv_capacity + a.num_splits - 1) / a.num_splits;
-
     int path = o.path;
-    if (path == GQA_PATH_AUTO) {
-        const int R = H / G;
-        if (decode_mfma_supports(a) && (R >= 8 || o.kv_dtype == DT_FP8)) path = GQA_PATH_MFMA;
-        else if (decode_valu_supports(a)) path = GQA_PATH_VALU;
-        else path = GQA_PATH_GENERIC;
-    }
+    if (path == GQA_PATH_AUTO) path = decode_mfma_supports(a) ? GQA_PATH_MFMA : GQA_PATH_GENERIC;
     if (path == GQA_PATH_VALU && !decode_valu_supports(a)) return GQA_ERR_UNSUPPORTED;
     if (path == GQA_PATH_MFMA && !decode_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
+
+    if (o.layout == GQA_LAYOUT_FLAT && !flat_possible(B, G, o.kv_capacity, path, o.num_splits))
+        return GQA_ERR_UNSUPPORTED;
+    const DecodePlan plan = plan_decode(B, H, G, D, o.kv_capacity, o.kv_dtype, o.num_splits, path, o.layout);
+    a.num_splits = plan.S;
+    a.split_len = plan.split_len;
+    a.flat = plan.flat;
+    a.flat_nw = plan.nw;
+    a.flat_cmin = plan.cmin;
 
     const size_t need = workspace_bytes_for(B, H, G, D, a.num_splits);
     if (need > 0 && o.workspace && o.workspace_bytes < need) return GQA_ERR_WORKSPACE;
@@ -215,7 +297,7 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
         a.counters = reinterpret_cast<int *>(base);
         a.part_acc = reinterpret_cast<float *>(base + counter_bytes(B, G));
         a.part_ml = reinterpret_cast<float *>(base + counter_bytes(B, G) + acc_bytes(B, H, D, a.num_splits));
-        a.fuse_combine = path != GQA_PATH_GENERIC && fuse_combine_for(H, G, D, a.num_splits);
+        a.fuse_combine = plan.fuse;
     }
 
     hipError_t e;
@@ -235,7 +317,7 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
     if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
     gqa_opts o;
     if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
-    if (o.reserved0 != 0) return GQA_ERR_INVALID_ARG;
+    if (o.layout < GQA_LAYOUT_AUTO || o.layout > GQA_LAYOUT_FLAT) return GQA_ERR_INVALID_ARG;
     if (B < 1 || T < 1 || H < 1 || G < 1 || D < 1 || H % G != 0 || D > kMaxDim) return GQA_ERR_INVALID_ARG;
     if ((double)B * H * (double)T * D > 9.0e15 || (double)B * G * H * (double)T > 2.0e9)
         return GQA_ERR_INVALID_ARG;

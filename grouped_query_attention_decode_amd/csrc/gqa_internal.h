@@ -26,8 +26,12 @@ struct AttnArgs {
     int Tk;                   // key rows allocated per (b, g): T_cap or T
     int causal;               // prefill: 1 = keys j <= i only
     int decode;               // 1 = keys limited by seq_lens[b], query at row L-1
-    int num_splits;           // decode: number of key ranges (1 = write out directly)
-    int split_len;            // decode: keys per range
+    int num_splits;           // decode: key ranges per (b, g) (1 = write out directly); with the
+                              // flat layout, the partial slots per query head
+    int split_len;            // decode, uniform layout: keys per range
+    int flat;                 // decode: 1 = flat layout of a ragged batch (splitkv.h)
+    int flat_nw;              // flat layout: workgroups of the decode kernel
+    int flat_cmin;            // flat layout: fewest rows per workgroup
     float scale_log2;         // scale * log2(e): scores are kept in the base-2 domain
     int q_dtype, kv_dtype;
 };

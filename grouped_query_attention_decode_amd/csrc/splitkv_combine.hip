@@ -14,6 +14,7 @@
 // the scalar cache) leave in one round trip. A row with no keys at all is 0.
 #include "dtypes.h"
 #include "gqa_internal.h"
+#include "splitkv.h"
 
 namespace gqa {
 
@@ -21,21 +22,60 @@ namespace {
 
 constexpr int kChunk = 32;  // ranges whose loads are in flight together
 
-// One workgroup per (sequence, query head); thread d owns head dim d.
-template <typename QT>
-__global__ __launch_bounds__(256) void splitkv_combine_kernel(const float *__restrict__ part_acc,
-                                                              const float *__restrict__ part_ml,
-                                                              QT *__restrict__ out, int S, int D) {
+// Flat layout (splitkv.h): the number of pieces of this row's (sequence, KV head) segment,
+// from the sequence lengths, by the whole workgroup.
+__device__ int flat_row_pieces(const AttnArgs &a, int b, int g) {
+    __shared__ int red_s[2][4];
+    int tot = 0, pre = 0;
+    for (int bb = threadIdx.x; bb < a.B; bb += blockDim.x) {
+        const int t = clamp_len(a.seq_lens[bb], a.Tk);
+        tot += t;
+        if (bb < b) pre += t;
+    }
+    tot = wave_sum(tot);
+    pre = wave_sum(pre);
+    const int wave = threadIdx.x >> 6, nwave = (blockDim.x + 63) >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red_s[0][wave] = tot;
+        red_s[1][wave] = pre;
+    }
+    __syncthreads();
+    int Ng = 0, Pb = 0;
+    for (int w = 0; w < nwave; ++w) {
+        Ng += red_s[0][w];
+        Pb += red_s[1][w];
+    }
+    Ng = __builtin_amdgcn_readfirstlane(Ng);
+    Pb = __builtin_amdgcn_readfirstlane(Pb);
+    const int C = flat_chunk(a.G * Ng, a.flat_nw, a.flat_cmin);
+    return flat_pieces(Ng, C, Pb, clamp_len(a.seq_lens[b], a.Tk), g);
+}
+
+// One workgroup per (sequence, query head); thread d owns head dim d. Uniform layout: all
+// S slots (an empty range left m = -inf); flat layout: the row's pieces, and nothing to do
+// for a row that one piece covered (the decode kernel wrote it).
+template <typename QT, bool FLAT>
+__global__ __launch_bounds__(256) void splitkv_combine_kernel(AttnArgs a) {
+    const float *__restrict__ part_acc = a.part_acc;
+    const float *__restrict__ part_ml = a.part_ml;
+    QT *__restrict__ out = static_cast<QT *>(a.out);
+    const int S = a.num_splits, D = a.D;
     const long bh = blockIdx.x;
+    int n = S;
+    if constexpr (FLAT) {
+        const int b = (int)(bh / a.H), g = (int)(bh % a.H) / (a.H / a.G);
+        n = flat_row_pieces(a, b, g);
+        if (n == 1) return;
+    }
     const int d = threadIdx.x < D ? threadIdx.x : D - 1;  // spare lanes load a valid dim
     const float *ml = part_ml + bh * S * 2;
     const float *acc = part_acc + bh * S * D + d;
     float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < S; s0 += kChunk) {
+    for (int s0 = 0; s0 < n; s0 += kChunk) {
         float m[kChunk], l[kChunk], x[kChunk];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            const int s = s0 + j < S ? s0 + j : S - 1;
+            const int s = s0 + j < n ? s0 + j : n - 1;
             m[j] = ml[2 * s];
             l[j] = ml[2 * s + 1];
             x[j] = acc[(long)s * D];
@@ -49,7 +89,7 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(const float *__res
         den *= alpha;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            const float w = (s0 + j < S && m[j] != -INFINITY) ? exp2f(m[j] - Mc) : 0.f;
+            const float w = (s0 + j < n && m[j] != -INFINITY) ? exp2f(m[j] - Mc) : 0.f;
             num += w != 0.f ? w * x[j] : 0.f;  // never 0 * (unwritten value)
             den += w * l[j];
         }
@@ -64,12 +104,13 @@ hipError_t launch_combine(const AttnArgs &a, hipStream_t stream) {
     if (a.D > 256) return hipErrorInvalidValue;
     dim3 grid((unsigned)(a.B * a.H));
     dim3 block((unsigned)((a.D + 63) / 64 * 64));
-    if (a.q_dtype == DT_F32)
-        hipLaunchKernelGGL(splitkv_combine_kernel<float>, grid, block, 0, stream, a.part_acc, a.part_ml,
-                           static_cast<float *>(a.out), a.num_splits, a.D);
-    else
-        hipLaunchKernelGGL(splitkv_combine_kernel<uint16_t>, grid, block, 0, stream, a.part_acc, a.part_ml,
-                           static_cast<uint16_t *>(a.out), a.num_splits, a.D);
+    if (a.q_dtype == DT_F32) {
+        if (a.flat) hipLaunchKernelGGL((splitkv_combine_kernel<float, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((splitkv_combine_kernel<float, false>), grid, block, 0, stream, a);
+    } else {
+        if (a.flat) hipLaunchKernelGGL((splitkv_combine_kernel<uint16_t, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((splitkv_combine_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -73,6 +73,19 @@ typedef enum gqa_path {
     GQA_PATH_MFMA = 3      /* matrix cores; bf16 or fp8 KV, bf16 q, D = 128 */
 } gqa_path;
 
+/* Decode work layout. UNIFORM cuts every (sequence, KV head) into the same number of key
+ * ranges (num_splits); FLAT lays the valid keys of all sequences end to end and gives every
+ * workgroup the same number of them, so a batch of very unequal lengths still keeps every
+ * compute unit busy (matrix-core family only, batches with B * G * kv_capacity < 2^31).
+ * AUTO takes FLAT for batches of 16 or more sequences on the matrix-core family and UNIFORM
+ * otherwise. The split-KV scheme these build on is the one of ["GQA revolution ...", section
+ * on split-KV block computation]; the flat layout is this library's own. */
+typedef enum gqa_layout {
+    GQA_LAYOUT_AUTO = 0,
+    GQA_LAYOUT_UNIFORM = 1,
+    GQA_LAYOUT_FLAT = 2
+} gqa_layout;
+
 typedef struct gqa_opts {
     size_t struct_size;     /* sizeof(gqa_opts); fields past it are taken as defaults */
     int32_t q_dtype;        /* gqa_dtype of q and out (default BF16) */
@@ -80,7 +93,7 @@ typedef struct gqa_opts {
     int32_t kv_capacity;    /* decode: T_cap, rows allocated per (sequence, KV head); required */
     int32_t num_splits;     /* decode: KV splits per (sequence, KV head); 0 = choose */
     int32_t path;           /* gqa_path (default AUTO) */
-    int32_t reserved0;      /* must be 0 */
+    int32_t layout;         /* decode: gqa_layout (default AUTO); FLAT excludes num_splits > 0 */
     const float *k_scale;   /* fp8 KV: device fp32 [B*G], index b*G + g; else NULL */
     const float *v_scale;   /* fp8 KV: device fp32 [B*G]; else NULL */
     void *workspace;        /* device scratch for split partials, or NULL */
@@ -88,7 +101,7 @@ typedef struct gqa_opts {
 } gqa_opts;
 
 /* Fill `opts` with defaults: struct_size set, BF16/BF16, kv_capacity 0 (must be set
- * for decode), num_splits 0, path AUTO, no scales, no workspace. */
+ * for decode), num_splits 0, path AUTO, layout AUTO, no scales, no workspace. */
 void gqa_opts_init(gqa_opts *opts);
 
 /*
@@ -143,13 +156,15 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
                        int H, int G, int D, float scale, int causal, hipStream_t stream,
                        const gqa_opts *opts);
 
-/* Number of KV splits gqa_decode uses for these sizes (num_splits 0 = the library's
- * own choice, which depends only on these arguments). Returns 0 for invalid sizes. */
+/* Key ranges per (sequence, KV head) -- with the flat layout, the most partial results one
+ * query head can have -- that gqa_decode uses for these sizes with path and layout AUTO
+ * (num_splits 0 = the library's own choice, which depends only on these arguments). Returns 0
+ * for invalid sizes. */
 int gqa_decode_num_splits(int B, int H, int G, int D, int kv_capacity, int kv_dtype,
                           int num_splits);
 
-/* Bytes of device workspace gqa_decode needs for these sizes; 0 when it needs none
- * (one split). Returns SIZE_MAX for invalid sizes. */
+/* Bytes of device workspace gqa_decode needs for these sizes, enough for every path and
+ * layout; 0 when it needs none (one split). Returns SIZE_MAX for invalid sizes. */
 size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, int kv_dtype,
                                  int num_splits);
 

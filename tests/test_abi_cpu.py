@@ -78,7 +78,10 @@ INV, UNS, WSP = 1, 2, 3
     (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
     (dict(num_splits=-1), INV), (dict(num_splits=1025), INV),
     (dict(path=4), INV), (dict(path=-1), INV),
-    (dict(reserved0=1), INV),
+    (dict(layout=3), INV), (dict(layout=-1), INV),
+    (dict(layout=2, num_splits=4), INV),                 # flat layout chooses its own ranges
+    (dict(layout=2, path=1), UNS),                       # flat layout: matrix-core path only
+    (dict(layout=2, q_dtype=0, kv_dtype=0), UNS),
     (dict(q_dtype=7), INV), (dict(kv_dtype=9), INV),
     (dict(q_dtype=0, kv_dtype=1), UNS),        # f32 q with bf16 cache
     (dict(q_dtype=1, kv_dtype=0), UNS),

@@ -1,9 +1,11 @@
 """Graph capture of the C-ABI calls (needs a gfx950 GPU).
 
-Decode (vector-ALU and matrix-core paths, split key ranges) and prefill are captured into a
-HIP graph on a side stream; the graph is replayed several times with unrelated eager work
-and synchronisations in between, and every replay must reproduce the eager result bit for
-bit (the kernels use no atomics, so results are deterministic).
+Decode (vector-ALU and matrix-core paths, split key ranges, both work layouts, merges in a
+second kernel or inside the decode kernel) and prefill are captured into a HIP graph on a side
+stream; the graph is replayed several times with unrelated eager work and synchronisations in
+between, and every replay must reproduce the eager result bit for bit: partial results are
+merged in a fixed order (the only atomics are integer arrival counters), and every replay
+reuses one workspace, so the counters must be back at zero after each call.
 """
 
 import pytest
@@ -33,19 +35,20 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("path,splits", [("valu", 8), ("mfma", 8), ("valu", 1)])
-def test_decode_graph_replays(gqa, path, splits):
+@pytest.mark.parametrize("path,splits,layout", [("valu", 8, "auto"), ("mfma", 8, "auto"), ("valu", 1, "auto"),
+                                                ("mfma", 0, "uniform"), ("mfma", 0, "flat")])
+def test_decode_graph_replays(gqa, path, splits, layout):
     d = "cuda"
-    c = W.make_decode(2, 32, 8, 128, [700, 1500], T_cap=1536, seed=31, name="graph")
+    c = W.make_decode(3, 32, 8, 128, [700, 1500, 0], T_cap=1536, seed=31, name="graph")
     q, kc, vc, sl = c.q.to(d), c.k_cache.to(d), c.v_cache.to(d), c.seq_lens.to(d)
     ws = torch.zeros(max(1, gqa.decode_workspace_size(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype, splits)),
                      dtype=torch.uint8, device=d)
-    ref = gqa.decode(q, kc, vc, sl, scale=c.scale, num_splits=splits, path=path, workspace=ws)
+    ref = gqa.decode(q, kc, vc, sl, scale=c.scale, num_splits=splits, path=path, workspace=ws, layout=layout)
     torch.cuda.synchronize()
     ref = ref.clone()
     out = torch.empty_like(q)
     g = _capture(lambda: gqa.decode(q, kc, vc, sl, out=out, scale=c.scale, num_splits=splits, path=path,
-                                    workspace=ws))
+                                    workspace=ws, layout=layout))
     other = W.make_decode(1, 16, 2, 128, [300], T_cap=320, seed=32, name="other")
     oq, ok, ov, osl = other.q.to(d), other.k_cache.to(d), other.v_cache.to(d), other.seq_lens.to(d)
     for rep in range(4):

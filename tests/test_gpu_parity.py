@@ -32,14 +32,14 @@ def gqa():
     return g
 
 
-def dev_decode(gqa, case, path="auto", num_splits=0, out=None):
+def dev_decode(gqa, case, path="auto", num_splits=0, out=None, layout="auto"):
     d = "cuda"
     ks = case.k_scale.to(d) if case.k_scale is not None else None
     vs = case.v_scale.to(d) if case.v_scale is not None else None
     _say(f"[gpu] decode {case.name} B{case.B} H{case.H} G{case.G} D{case.D} T_cap{case.T_cap} "
-         f"kv={case.kv_dtype} path={path} splits={num_splits}")
+         f"kv={case.kv_dtype} path={path} splits={num_splits} layout={layout}")
     o = gqa.decode(case.q.to(d), case.k_cache.to(d), case.v_cache.to(d), case.seq_lens.to(d), out=out,
-                   scale=case.scale, k_scale=ks, v_scale=vs, num_splits=num_splits, path=path)
+                   scale=case.scale, k_scale=ks, v_scale=vs, num_splits=num_splits, path=path, layout=layout)
     torch.cuda.synchronize()
     return o
 
@@ -77,19 +77,24 @@ def supported(gqa, case, path):
 
 
 def run_all_paths(gqa, case, want, splits=(0,)):
+    """Every kernel family that takes these shapes, at each split count; with the library's own
+    split choice (0) the matrix-core family also runs in both work layouts."""
     ran = 0
     for path in DECODE_PATHS:
         if not supported(gqa, case, path):
             continue
-        for s in splits:
+        runs = [(s, "auto") for s in splits]
+        if path == "mfma" and 0 in splits:
+            runs += [(0, "uniform"), (0, "flat")]
+        for s, layout in runs:
             try:
-                got = dev_decode(gqa, case, path=path, num_splits=s)
+                got = dev_decode(gqa, case, path=path, num_splits=s, layout=layout)
             except gqa.GqaError as e:
                 if e.status == 2 and path != "generic":   # kernel family not built for these shapes
                     _say(f"    {path}: unsupported, skipped")
                     break
                 raise
-            check(got, want, TOL[case.kv_dtype], f"{case.name} path={path} splits={s}")
+            check(got, want, TOL[case.kv_dtype], f"{case.name} path={path} splits={s} layout={layout}")
             ran += 1
     assert ran > 0
 
@@ -161,6 +166,13 @@ DECODE_CASES = [
     (1, 12, 3, 64, [517], 600, W.BF16, W.BF16),              # head dim 64 (generic)
     (2, 6, 3, 80, [40, 3], 41, W.F32, W.F32),                # odd sizes, fp32
     (1, 4, 2, 3, [7], 7, W.F32, W.F32),
+    # Batches of many ragged sequences (the balanced flat layout of the matrix-core path):
+    # more than 64 sequences, empty ones and one-key ones among them.
+    (70, 8, 2, 128, [0 if i % 9 == 4 else (1 if i % 11 == 3 else (i * 37) % 300 + 1) for i in range(70)],
+     300, W.BF16, W.BF16),
+    (67, 32, 1, 128, [0 if i % 7 == 2 else (i * 53) % 200 + 1 for i in range(67)], 200, W.BF16, W.FP8),
+    (5, 64, 1, 128, [700, 0, 1, 333, 64], 700, W.BF16, W.BF16),   # 64 heads per KV head
+    (4, 16, 2, 128, [0, 0, 0, 0], 50, W.BF16, W.BF16),             # no keys at all
 ]
 
 
@@ -200,18 +212,18 @@ def test_decode_scale_and_constant_values(gqa):
 
 def test_decode_deterministic(gqa):
     c = W.make_decode(4, 32, 8, 128, "uniform:1:3000", T_cap=3000, seed=11, name="determinism")
-    for path in DECODE_PATHS:
+    for path, layout in [(p, "auto") for p in DECODE_PATHS] + [("mfma", "flat")]:
         if not supported(gqa, c, path):
             continue
         try:
-            a = dev_decode(gqa, c, path=path).clone()
+            a = dev_decode(gqa, c, path=path, layout=layout).clone()
         except gqa.GqaError as e:
             if e.status == 2:
                 continue
             raise
         for _ in range(3):
-            b = dev_decode(gqa, c, path=path)
-            assert torch.equal(a, b), f"path {path} not bitwise reproducible"
+            b = dev_decode(gqa, c, path=path, layout=layout)
+            assert torch.equal(a, b), f"path {path} layout {layout} not bitwise reproducible"
 
 
 # ---------------------------------------------------------------------------------------
