@@ -1,17 +1,19 @@
-// Wide-group GQA decode on the matrix cores (bf16 or fp8-E4M3FN KV cache, D = 128).
+// GQA decode on the matrix cores (bf16 or fp8-E4M3FN KV cache, D = 128, any R = H/G <= 64).
 //
-// With R = H/G query heads per KV head, decode does 4*R flops per cached element: at R >= 8
-// (and for MQA, R = 32, with fp8 storage) the vector ALUs cannot keep up with HBM, so both
-// contractions run as bf16 MFMA. Each KV row is read from HBM exactly once per (sequence,
-// KV head) and multiplied against all R query heads of its group inside one MFMA -- the
-// group sharing that defines GQA [GQA paper digest page (51969.com), section "Grouped-query
-// attention (GQA)"; the KV head of query head h is h / (H/G), "LLM principles -- code
-// implementation of multi-head attention (MQA and GQA)", section 5].
+// Both contractions run as bf16 MFMA, even for narrow groups (R = 4), where most MFMA rows
+// are padding: a decode step is latency-bound per wave, and the matrix cores finish a block
+// in about a third of the instructions the vector ALUs need. Each KV row is read from HBM
+// exactly once per (sequence, KV head) and multiplied against all R query heads of its group
+// inside one MFMA -- the group sharing that defines GQA [GQA paper digest page (51969.com),
+// section "Grouped-query attention (GQA)"; the KV head of query head h is h / (H/G), "LLM
+// principles -- code implementation of multi-head attention (MQA and GQA)", section 5].
 //
-// Work: one workgroup (4 waves) per (sequence b, KV head g, key range). Each wave streams
-// its own 32-token blocks of the range (blocks wave, wave+4, ...), keeping an independent
-// online-softmax state; the four states are merged at the end, and a split range leaves
-// (acc, max, sum) partials for the log-sum-exp combine kernel.
+// Work: a workgroup (4 waves) attends to one key range of one (sequence b, KV head g). Each
+// wave streams its own 32-token blocks of the range (blocks wave, wave+4, ...), keeping an
+// independent online-softmax state; the four states are merged at the end, and a split
+// range leaves (acc, max, sum) partials for the log-sum-exp merge (splitkv.h). Key ranges
+// come from one of two layouts: uniform (grid = range x sequence x KV head) or flat (equal
+// runs of the concatenated valid keys of all segments, splitkv.h).
 //
 // Per 32-token block, per wave:
 //   S^T (32 tokens x 16 heads per head block) = K . Q^T          -- 16x16x32 bf16 MFMA

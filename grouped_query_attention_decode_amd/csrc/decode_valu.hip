@@ -1,8 +1,10 @@
 // Narrow-group GQA decode on the vector ALUs (bf16 KV cache, D = 128, R = H/G <= 8).
 //
 // With few query heads per KV head (R = 4 for a GQA-8 model with 32 query heads) decode
-// does only 4*R flops per cached bf16 element, which the vector ALUs sustain at HBM rate;
-// matrix cores would mostly multiply padding. Each KV row is read once per (sequence,
+// does only 4*R flops per cached bf16 element, which the vector ALUs sustain at HBM rate.
+// The library's default is still the matrix-core kernel, whose per-block instruction count
+// is lower; this kernel is an independent second implementation, selected explicitly
+// (GQA_PATH_VALU) and checked against the same inputs. Each KV row is read once per (sequence,
 // KV head) and used for all R heads of the group [GQA paper digest page (51969.com),
 // section "Grouped-query attention (GQA)"; group of head h is h / (H/G), "LLM principles --
 // code implementation of multi-head attention (MQA and GQA)", section 5].

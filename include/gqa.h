@@ -26,7 +26,8 @@
  *
  * Execution: both compute calls only enqueue work on `stream` and return without
  * waiting; `out` is valid once the stream has drained. Results are deterministic
- * for fixed arguments (no floating-point atomics).
+ * for fixed arguments: partial results are merged in a fixed order (the only atomics are
+ * integer arrival counters).
  *
  * Errors: every call returns a gqa_status by value and never aborts or prints.
  * All argument checks run on the host before any HIP call, so a rejected call has
@@ -64,8 +65,8 @@ typedef enum gqa_dtype {
     GQA_DTYPE_FP8_E4M3FN = 2
 } gqa_dtype;
 
-/* Kernel family for decode. AUTO picks by shape; the others force a family so tests
- * can check each against the same inputs. */
+/* Kernel family for decode. AUTO takes MFMA wherever it applies and GENERIC otherwise;
+ * the others force a family so tests can check each against the same inputs. */
 typedef enum gqa_path {
     GQA_PATH_AUTO = 0,
     GQA_PATH_GENERIC = 1,  /* any head dim 1..256, any supported dtype pair */
