@@ -165,6 +165,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
                 const i32x4_t ka = *(const i32x4_t *)(kt + r * kRowBytes + 16 * ((2 * ks + hl) ^ swz(r)));
                 s[kh] = mfma32x32x16(ka, qT[ks], s[kh]);
             }
+        // K-operand reads lead their MFMAs by two k-steps, so their LDS latency overlaps
+        // MFMAs instead of stalling each pair (measured +2-3 % on the causal 2048 prefill).
+        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // LDS reads
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
         // ---- mask (diagonal / tail tiles only) and tile max on the raw scores ----
         if (need_mask) {
 #pragma unroll
