@@ -76,6 +76,10 @@ class Oracle:
         lib.gqa_oracle_prefill_rows.restype = ctypes.c_int
         lib.gqa_oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
         lib.gqa_oracle_e4m3fn_value.restype = ctypes.c_double
+        lib.gqa_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+        lib.gqa_oracle_e4m3fn_encode.restype = ctypes.c_uint8
+        lib.gqa_oracle_quant_e4m3fn.argtypes = [_fp, ctypes.c_float, ctypes.c_long, _u8p]
+        lib.gqa_oracle_quant_e4m3fn.restype = None
         lib.gqa_oracle_dequant_e4m3fn.argtypes = [_u8p, _fp, ctypes.c_long, ctypes.c_long, _dp]
         lib.gqa_oracle_dequant_e4m3fn.restype = None
         lib.gqa_oracle_num_threads.restype = ctypes.c_int
@@ -93,6 +97,41 @@ class Oracle:
     # ---- fp8 -----------------------------------------------------------------------
     def e4m3fn_value(self, code: int) -> float:
         return float(self.lib.gqa_oracle_e4m3fn_value(int(code) & 0xFF))
+
+    def e4m3fn_encode(self, q: float) -> int:
+        return int(self.lib.gqa_oracle_e4m3fn_encode(float(q)))
+
+    def quant_e4m3fn(self, x, scale: float) -> np.ndarray:
+        """Codes (uint8) of x / scale, the quotient in fp32, nearest-even, saturating at 448."""
+        xn = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        codes = np.empty(xn.shape, dtype=np.uint8)
+        self.lib.gqa_oracle_quant_e4m3fn(_ptr(xn, _fp), ctypes.c_float(float(np.float32(scale))), xn.size,
+                                         _ptr(codes, _u8p))
+        return codes
+
+    # ---- cache append ---------------------------------------------------------------
+    def append(self, case, k_new, v_new):
+        """The caches of a decode case after storing the new token's key and value [B, G, D]
+        (q's dtype) at row L_b - 1 of every (b, g) with 1 <= L_b <= T_cap: copied for fp32 and
+        bf16 caches, quantised with the slab's fixed scale for fp8 ones. Returns new cache
+        tensors (same dtype as the case's); the case is not modified."""
+        kc, vc = case.k_cache.clone(), case.v_cache.clone()
+        B, G, T_cap, D = kc.shape
+        kn = k_new.detach().cpu().to(torch.float32).numpy()
+        vn = v_new.detach().cpu().to(torch.float32).numpy()
+        for b in range(B):
+            L = int(case.seq_lens[b])
+            if not 1 <= L <= T_cap:
+                continue
+            for g in range(G):
+                if case.kv_dtype == "fp8_e4m3fn":
+                    i = b * G + g
+                    kc.view(torch.uint8)[b, g, L - 1] = torch.from_numpy(self.quant_e4m3fn(kn[b, g], case.k_scale[i]))
+                    vc.view(torch.uint8)[b, g, L - 1] = torch.from_numpy(self.quant_e4m3fn(vn[b, g], case.v_scale[i]))
+                else:
+                    kc[b, g, L - 1] = k_new[b, g].to(kc.dtype)
+                    vc[b, g, L - 1] = v_new[b, g].to(vc.dtype)
+        return kc, vc
 
     def dequant_e4m3fn(self, codes: torch.Tensor, scales: torch.Tensor) -> np.ndarray:
         """codes [S, ...] float8_e4m3fn (or uint8), scales [S] float32 -> float64 code*scale."""
@@ -212,5 +251,8 @@ def prefill_rows(case, rows, f64=None): return load().prefill_rows(case, rows, f
 def prefill_arrays(*a): return load().prefill_arrays(*a)
 def dequant_e4m3fn(codes, scales): return load().dequant_e4m3fn(codes, scales)
 def e4m3fn_value(code): return load().e4m3fn_value(code)
+def e4m3fn_encode(q): return load().e4m3fn_encode(q)
+def quant_e4m3fn(x, scale): return load().quant_e4m3fn(x, scale)
+def append(case, k_new, v_new): return load().append(case, k_new, v_new)
 def num_threads(): return load().num_threads()
 def set_num_threads(n): return load().set_num_threads(n)

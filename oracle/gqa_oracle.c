@@ -250,6 +250,39 @@ double gqa_oracle_e4m3fn_value(uint8_t code)
     return sign ? -mag : mag;
 }
 
+/* Quantise one value to OCP E4M3FN: the finite code whose value is nearest to q, ties to
+ * the code with an even mantissa (its last bit clear), the sign kept (a negative q that
+ * rounds to zero gives the code of -0). Magnitudes beyond the largest code, 448, give 448:
+ * a cache with fixed per-(sequence, KV head) scales saturates tokens that outgrow them
+ * (reading; "GQA revolution ...", section on mixed-precision KV storage, stores code *
+ * scale but does not say what happens out of range). NaN gives the NaN code 0x7F.
+ * Written as an exhaustive search over the 127 non-negative finite codes. */
+uint8_t gqa_oracle_e4m3fn_encode(float q)
+{
+    if (isnan(q)) return 0x7F;
+    const int neg = signbit(q) ? 1 : 0;
+    const double a = fabs((double)q);
+    int best = 0;
+    double best_err = INFINITY;
+    int c;
+    for (c = 0; c <= 0x7E; ++c) {
+        /* differences of a float and a 4-significant-bit value are exact in double */
+        const double err = fabs(a - gqa_oracle_e4m3fn_value((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+/* Quantise n values: codes[i] = encode(x[i] / scale), the quotient taken in fp32. */
+void gqa_oracle_quant_e4m3fn(const float *x, float scale, long n, uint8_t *codes)
+{
+    long i;
+    for (i = 0; i < n; ++i) codes[i] = gqa_oracle_e4m3fn_encode(x[i] / scale);
+}
+
 /* Dequantise fp8 slabs: out[s][i] = value(codes[s][i]) * scales[s], s < nslab, i < slab_len. */
 void gqa_oracle_dequant_e4m3fn(const uint8_t *codes, const float *scales, long nslab,
                                long slab_len, double *out)

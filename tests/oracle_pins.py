@@ -307,7 +307,31 @@ def pin_e4m3fn_decoder(orc):
     assert np.array_equal(deq[1][~nan_w[128:]], want[128:][~nan_w[128:]] * 3.0)
 
 
+def pin_e4m3fn_encoder(orc):
+    """The encoder against the format and a library cast: every finite code round-trips,
+    every midpoint between neighbouring codes goes to the even one, values beyond 448
+    saturate, and values inside the range match torch's float8_e4m3fn cast (nearest even);
+    the quotient x / scale is taken in fp32."""
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    for c in finite:
+        assert orc.e4m3fn_encode(orc.e4m3fn_value(c)) == c, f"round trip {c:#x}"
+    pos = sorted(finite[:127], key=orc.e4m3fn_value)
+    for lo, hi in zip(pos, pos[1:]):
+        mid = (orc.e4m3fn_value(lo) + orc.e4m3fn_value(hi)) / 2
+        even = lo if (lo & 1) == 0 else hi
+        assert orc.e4m3fn_encode(mid) == even and orc.e4m3fn_encode(-mid) == even | 0x80, f"midpoint {lo:#x}"
+    for big in (449.0, 1e6):
+        assert orc.e4m3fn_encode(big) == 0x7E and orc.e4m3fn_encode(-big) == 0xFE, "saturation"
+    g = torch.Generator().manual_seed(11)
+    x = torch.cat([torch.randn(4000, generator=g) * 60, (torch.rand(1000, generator=g) * 2 - 1) * 448])
+    want = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.quant_e4m3fn(x.numpy(), 1.0), want), "library cast"
+    q = np.float32(np.float32(1.3) / np.float32(0.37))
+    assert orc.quant_e4m3fn([np.float32(1.3)], np.float32(0.37))[0] == orc.e4m3fn_encode(q), "fp32 quotient"
+
+
 ALL_PINS = [pin_hand_worked, pin_toy_three_ways, pin_sdpa_prefill, pin_sdpa_decode, pin_mha, pin_mqa,
             pin_group_materialise, pin_identical_keys_mean_v, pin_value_constant_per_head, pin_single_row,
             pin_shift_invariance, pin_permutation_invariance, pin_linear_and_convex,
-            pin_incremental_decode_equals_prefill, pin_nan_padding, pin_length_readings, pin_e4m3fn_decoder]
+            pin_incremental_decode_equals_prefill, pin_nan_padding, pin_length_readings, pin_e4m3fn_decoder,
+            pin_e4m3fn_encoder]

@@ -21,6 +21,10 @@ MUTANTS = [
     ("batch_group_swap", "((long)b * G + g) * T_cap * D", "((long)g * B + b) * T_cap * D"),
     ("fp8_bias", "e - 7);", "e - 8);"),
     ("fp8_subnormal", "(double)m / 8.0, -6);", "(double)m / 8.0, -7);"),
+    ("fp8_ties_to_odd", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    ("fp8_quotient_inverted", "codes[i] = gqa_oracle_e4m3fn_encode(x[i] / scale);",
+     "codes[i] = gqa_oracle_e4m3fn_encode(x[i] * scale);"),
+    ("fp8_sign_dropped", "return (uint8_t)(best | (neg << 7));", "return (uint8_t)best;"),
 ]
 
 
