@@ -50,6 +50,8 @@ class GqaOpts(ctypes.Structure):
         ("v_scale", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
     ]
 
 
@@ -143,11 +145,15 @@ def _stream_handle(stream, device) -> int:
 
 
 def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
-           num_splits=0, path="auto", workspace=None, stream=None, layout="auto"):
+           num_splits=0, path="auto", workspace=None, stream=None, layout="auto", k_new=None, v_new=None):
     """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype).
 
     ``layout`` ("auto", "uniform" or "flat") chooses how the key rows are spread over the
     workgroups; "flat" balances batches of unequal lengths (matrix-core path only).
+
+    ``k_new``/``v_new`` ([B, G, D], q's dtype; both or neither) append the current token to the
+    caches first: row seq_lens[b]-1 of every (b, g) with 1 <= seq_lens[b] <= T_cap receives them
+    (E4M3FN codes of k_new / k_scale for fp8 caches), and the attention includes that row.
 
     ``workspace`` (uint8 device tensor of at least ``decode_workspace_size`` bytes) must be
     zero-filled before its first use; each completed call leaves it ready for the next.
@@ -178,6 +184,14 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
             if t.dtype != torch.float32 or t.numel() != B * G:
                 raise ValueError(f"{n} must be float32 [B*G]")
         o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _need_cuda(t, n)
+            if t.dtype != q.dtype or tuple(t.shape) != (B, G, D):
+                raise ValueError(f"{n} must be [B, G, D] = {(B, G, D)} in q's dtype")
+        o.k_new, o.v_new = k_new.data_ptr(), v_new.data_ptr()
     need = decode_workspace_size(B, H, G, D, T_cap, kv_code, int(num_splits))
     if need > 0:
         if workspace is None:

@@ -24,6 +24,7 @@ SOURCES = [
     "gqa_api.hip",
     "attn_generic.hip",
     "splitkv_combine.hip",
+    "kv_append.hip",
     "decode_valu.hip",
     "decode_mfma.hip",
     "prefill_mfma.hip",

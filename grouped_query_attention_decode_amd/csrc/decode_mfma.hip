@@ -28,6 +28,8 @@
 // Tokens at or beyond the valid length are masked by index; their rows are never loaded
 // (the load index is clamped to the last valid row, and their probabilities are zero).
 // v_scale multiplies the output once, in the epilogue.
+// With a cache append, the wave whose block holds the last valid row swaps the caller's new
+// key/value (quantised for fp8) into its registers and stores that row: no separate pass.
 #include "dtypes.h"
 #include "gqa_internal.h"
 #include "mfma_util.h"
@@ -108,11 +110,79 @@ __device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp
     }
 }
 
+// Cache append inside the attention: the block starting at t0 holds row r, the last valid
+// row, which the caller's current key and value (bf16, [B*G][128]) replace. The lanes whose
+// registers hold a 16-byte chunk of row r -- every chunk sits in exactly one lane, in the K
+// operand layout and in the V row layout alike -- put the new chunk (quantised for an fp8
+// cache) in its place and store it to the cache, so the row is written once and attended to
+// with exactly the bytes stored.
+template <bool FP8>
+__device__ __forceinline__ void append_row(Frag<FP8> &f, const AttnArgs &a, int bg, const char *kbase,
+                                           const char *vbase, int t0, int r, int lane) {
+    constexpr int RB = FP8 ? 128 : 256;
+    const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (long)bg * kD;
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (long)bg * kD;
+    char *kr = const_cast<char *>(kbase) + (long)r * RB;
+    char *vr = const_cast<char *>(vbase) + (long)r * RB;
+    const int rb = r - t0;  // row in the block, 0..31
+    // Registers are chosen by per-lane predicates over compile-time indices, so that the
+    // fragment stays in registers.
+    if constexpr (FP8) {
+        // The wave quantises the 256 new values once, four per lane (K dims 4l .. 4l+3 in lanes
+        // 0-31, V dims in lanes 32-63), and each lane gathers the four words of its chunks.
+        const int hl = lane & 31;
+        const i32x2_t w = *(const i32x2_t *)((lane < 32 ? kn : vn) + 4 * hl);
+        const float sc = lane < 32 ? a.k_scale[bg] : a.v_scale[bg];
+        const int word = (int)quant_e4m3fn_x4(__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
+                                              __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u), sc);
+        auto gather = [&](int l0) { return i32x4_t{__shfl(word, l0), __shfl(word, l0 + 1), __shfl(word, l0 + 2), __shfl(word, l0 + 3)}; };
+        i32x4_t kc[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) kc[p] = gather((64 * p + 16 * (lane >> 4)) / 4);
+        const i32x4_t vc = gather(32 + 4 * (lane & 7));
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+                if (tau(blk, lane & 15) == rb) {
+                    f.k[blk * 2 + p] = kc[p];
+                    *(i32x4_t *)(kr + 64 * p + 16 * (lane >> 4)) = kc[p];
+                }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (8 * i + (lane >> 3) == rb) {
+                f.v[i] = vc;
+                *(i32x4_t *)(vr + 16 * (lane & 7)) = vc;
+            }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int d0 = 32 * kk + 8 * (lane >> 4);
+            const i32x4_t x = *(const i32x4_t *)(kn + d0);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+                if (tau(blk, lane & 15) == rb) {
+                    f.k[blk * 4 + kk] = x;
+                    *(i32x4_t *)(kr + 2 * d0) = x;
+                }
+        }
+        const int d0 = 8 * (lane & 15);
+        const i32x4_t x = *(const i32x4_t *)(vn + d0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (4 * i + (lane >> 4) == rb) {
+                f.v[i] = x;
+                *(i32x4_t *)(vr + 2 * d0) = x;
+            }
+    }
+}
+
 // Where one call of attend() leaves its result.
 struct PieceOut {
     int slot;     // partial slot of this key range
     int n_slots;  // key ranges of this (sequence, KV head) that hold keys
     bool direct;  // the range covers the whole sequence: write the output itself
+    bool append;  // the range ends at the sequence's last row, which the new token fills
 };
 
 // Attention of query heads head0 .. head0+R-1 over key rows kb .. ke-1 of one (sequence, KV
@@ -272,7 +342,15 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         }
         };
     constexpr int kStep = kWaves * kBlockT;
-    for (int t0 = kb + wave * kBlockT; t0 < ke; t0 += kStep) step(nxt, t0, kStep);
+    int t0 = kb + wave * kBlockT;
+    if (t0 < ke) {
+        // The wave's last block is peeled off the loop: it is the one that may hold the row
+        // of a cache append, and code for that kept out of the loop costs it no registers.
+        const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
+        for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep);
+        if (po.append && tl + kBlockT >= ke) append_row<FP8>(nxt, a, bg, kbase, vbase, tl, ke - 1, lane);
+        step(nxt, tl, kStep);
+    }
 
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
     // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
@@ -373,7 +451,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     Frag<FP8> nxt;
     if (kb + wave * kBlockT < a.Tk) load_block<FP8>(nxt, kbase, vbase, kb + wave * kBlockT, a.Tk, lane);
 
-    const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Tk));
+    const int Lraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    const int L = clamp_len(Lraw, a.Tk);
     const int ke = kb + a.split_len < L ? kb + a.split_len : L;
 
     if (kb >= ke) {  // nothing to attend to in this range
@@ -395,6 +474,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     po.n_slots = active_splits(L, a.split_len, S);
     // With the in-kernel merge, a sequence whose keys all fall in this range needs no merge.
     po.direct = S == 1 || (a.fuse_combine && po.n_slots == 1);
+    po.append = a.k_new && ke == L && Lraw == L;  // Lraw in 1..T_cap: the row exists
     attend<NHB, FP8>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, kbase, vbase,
                      a.scale_log2 * kscale, vscale);
 }
@@ -458,7 +538,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_k
     const int xe = x + C < N ? x + C : N;
     int g = gb0 / B, b = gb0 % B;
     while (x < xe) {
-        const int Tb = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Tk));
+        const int Tbraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+        const int Tb = clamp_len(Tbraw, a.Tk);
         const int s0 = g * Ng + Pb;  // first row of segment (b, g)
         if (x >= s0 + Tb) {          // segment done (or empty): next one
             Pb += Tb;
@@ -477,6 +558,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_k
         po.n_slots = flat_pieces(Ng, C, Pb, Tb, g);
         po.slot = (int)blockIdx.x - (int)((unsigned)s0 / (unsigned)C);
         po.direct = po.n_slots == 1;
+        po.append = a.k_new && ke == Tb && Tbraw == Tb;
 
         i32x4_t qT[NHB][4];
         load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);

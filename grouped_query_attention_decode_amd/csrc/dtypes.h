@@ -36,6 +36,21 @@ template <> struct KvElem<0> { using T = float; };
 template <> struct KvElem<1> { using T = uint16_t; };
 template <> struct KvElem<2> { using T = uint8_t; };
 
+// Cache append for fp8 slabs with a fixed scale: the E4M3FN code of the fp32 quotient x / scale,
+// magnitudes beyond the largest code (448) saturated, NaN to the NaN code 0x7F; the hardware
+// conversion rounds to nearest, ties to even (it gives 0xFF for every NaN, so those bytes are
+// replaced). Packs four codes (byte i = code of x[i]).
+__device__ __forceinline__ uint32_t quant_e4m3fn_x4(float x0, float x1, float x2, float x3, float scale) {
+    const float q0 = x0 / scale, q1 = x1 / scale, q2 = x2 / scale, q3 = x3 / scale;
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(q0, -448.f), 448.f), fminf(fmaxf(q1, -448.f), 448.f),
+                                                   0, false);  // bytes 0, 1
+    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(q2, -448.f), 448.f),
+                                                                 fminf(fmaxf(q3, -448.f), 448.f), lo, true);  // bytes 2, 3
+    const uint32_t nan = (q0 != q0 ? 0xFFu : 0u) | (q1 != q1 ? 0xFF00u : 0u) | (q2 != q2 ? 0xFF0000u : 0u) |
+                         (q3 != q3 ? 0xFF000000u : 0u);
+    return (c & ~nan) | (0x7F7F7F7Fu & nan);
+}
+
 __device__ __forceinline__ float load_f32(const float *p, long i) { return p[i]; }
 __device__ __forceinline__ float load_f32(const uint16_t *p, long i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float load_f32(const uint8_t *p, long i) { return e4m3fn_to_f32(p[i]); }

@@ -2,8 +2,9 @@
 //
 // Every check runs before the first HIP call, so a rejected call leaves the device and
 // the stream untouched. The launch sequence is: (optional) stream-ordered workspace,
-// the attention kernel, the split-KV combine when the cache was split, and the release
-// of the workspace -- all on the caller's stream, with no host synchronisation.
+// the cache append when it is not fused, the attention kernel, the split-KV combine when
+// the cache was split, and the release of the workspace -- all on the caller's stream,
+// with no host synchronisation.
 #include <math.h>
 #include <stddef.h>
 #include <string.h>
@@ -248,6 +249,7 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
                          (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8);
     if (!pair_ok) return GQA_ERR_UNSUPPORTED;
     if (o.kv_dtype == DT_FP8 && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+    if ((o.k_new == nullptr) != (o.v_new == nullptr)) return GQA_ERR_INVALID_ARG;
 
     AttnArgs a;
     memset(&a, 0, sizeof(a));
@@ -300,10 +302,23 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
         a.fuse_combine = plan.fuse;
     }
 
-    hipError_t e;
-    if (path == GQA_PATH_MFMA) e = launch_decode_mfma(a, stream);
-    else if (path == GQA_PATH_VALU) e = launch_decode_valu(a, stream);
-    else e = launch_generic(a, stream);
+    hipError_t e = hipSuccess;
+    if (o.k_new) {
+        // The matrix-core kernel stores the new row itself, from the registers it attends with
+        // (its 16-byte loads need 16-byte aligned rows); every other case copies it first.
+        const bool fused = path == GQA_PATH_MFMA && ((uintptr_t)o.k_new % 16) == 0 && ((uintptr_t)o.v_new % 16) == 0;
+        a.k_new = o.k_new;
+        a.v_new = o.v_new;
+        if (!fused) {
+            e = launch_kv_append(a, stream);
+            a.k_new = a.v_new = nullptr;
+        }
+    }
+    if (e == hipSuccess) {
+        if (path == GQA_PATH_MFMA) e = launch_decode_mfma(a, stream);
+        else if (path == GQA_PATH_VALU) e = launch_decode_valu(a, stream);
+        else e = launch_generic(a, stream);
+    }
     if (e == hipSuccess && a.num_splits > 1 && !a.fuse_combine) e = launch_combine(a, stream);
     if (owned) {
         const hipError_t f = hipFreeAsync(ws, stream);

@@ -19,6 +19,8 @@ struct AttnArgs {
     const float *v_scale;
     float *part_acc;          // split partials, [B*H][S][D] (unnormalised)
     float *part_ml;           // split partials, [B*H][S][2] = (running max, running sum)
+    const void *k_new;        // decode with append: the current token's key [B*G][D] (q's dtype)
+    const void *v_new;        //   and value; both null without append
     int *counters;            // split arrival counters, [B*G], zero between calls
     int fuse_combine;         // 1: the last workgroup of each (b, g) merges the partials
     int B, H, G, D;
@@ -41,6 +43,7 @@ hipError_t launch_combine(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_kv_append(const AttnArgs &a, hipStream_t stream);
 
 // Shape limits of the fast kernels (checked on the host before launch).
 bool decode_valu_supports(const AttnArgs &a);

@@ -1,0 +1,49 @@
+// Cache append as its own kernel, for the decode families that do not fuse it (generic and
+// vector-ALU): the current token's key and value, [B*G][D] in q's dtype, are stored at row
+// L_b - 1 of every (b, g) with 1 <= L_b <= T_cap ("LLM principles -- code implementation of
+// multi-head attention (MQA and GQA)", sections 3 and 5: the new K/V are appended to the
+// cache before the scores). fp32 and bf16 caches take the values unchanged; fp8 caches take
+// E4M3FN codes of x / scale with the slab's fixed scale, saturated at 448 ("GQA revolution:
+// how xformers speeds up LLM inference", section on mixed-precision KV storage).
+#include "dtypes.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+
+namespace {
+
+// One workgroup per (b, g); thread d handles head dim d.
+template <typename QT, typename KT, bool FP8>
+__global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a) {
+    const int bg = blockIdx.x;
+    const int b = bg / a.G;
+    const int L = a.seq_lens[b];
+    const int d = threadIdx.x;
+    if (L < 1 || L > a.Tk || d >= a.D) return;
+    const long i = ((long)bg * a.Tk + (L - 1)) * a.D + d;
+    const float k = load_f32(static_cast<const QT *>(a.k_new), (long)bg * a.D + d);
+    const float v = load_f32(static_cast<const QT *>(a.v_new), (long)bg * a.D + d);
+    if constexpr (FP8) {
+        static_cast<uint8_t *>(const_cast<void *>(a.k))[i] = (uint8_t)quant_e4m3fn_x4(k, 0.f, 0.f, 0.f, a.k_scale[bg]);
+        static_cast<uint8_t *>(const_cast<void *>(a.v))[i] = (uint8_t)quant_e4m3fn_x4(v, 0.f, 0.f, 0.f, a.v_scale[bg]);
+    } else {
+        store_f32(static_cast<KT *>(const_cast<void *>(a.k)), i, k);  // exact: same type
+        store_f32(static_cast<KT *>(const_cast<void *>(a.v)), i, v);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AttnArgs &a, hipStream_t stream) {
+    if (a.D > 256) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.B * a.G)), block(256);
+    if (a.kv_dtype == DT_F32)
+        hipLaunchKernelGGL((kv_append_kernel<float, float, false>), grid, block, 0, stream, a);
+    else if (a.kv_dtype == DT_BF16)
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t, uint16_t, false>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t, uint8_t, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gqa

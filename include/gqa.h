@@ -99,6 +99,8 @@ typedef struct gqa_opts {
     const float *v_scale;   /* fp8 KV: device fp32 [B*G]; else NULL */
     void *workspace;        /* device scratch for split partials, or NULL */
     size_t workspace_bytes; /* size of `workspace` */
+    const void *k_new;      /* decode: the current token's key [B, G, D] (q's dtype) to append, or NULL */
+    const void *v_new;      /* decode: its value [B, G, D]; set both or neither */
 } gqa_opts;
 
 /* Fill `opts` with defaults: struct_size set, BF16/BF16, kv_capacity 0 (must be set
@@ -132,6 +134,19 @@ void gqa_opts_init(gqa_opts *opts);
  * zero-filled before its first use (it holds per-(sequence, KV head) arrival counters);
  * every completed call leaves it ready for the next one. Calls that run concurrently must
  * not share a workspace.
+ *
+ * Cache append (optional): with opts->k_new and opts->v_new set, the call first stores the
+ * current token's key and value at row seq_lens[b]-1 of every (b, g) whose length lies in
+ * 1..T_cap, then attends over rows 0..seq_lens[b]-1 as above, the stored row included; the
+ * caller then need not write the row itself ("LLM principles -- code ...", sections 3 and 5
+ * append the new K/V to the cache before the scores). fp32 and bf16 caches receive the values
+ * unchanged; an fp8 cache receives the E4M3FN code nearest (ties to even) to the fp32 quotient
+ * k_new / k_scale[b*G+g] (v likewise), with the slab's scale kept fixed: magnitudes beyond 448
+ * saturate ["GQA revolution ...", section on mixed-precision KV storage, stores code * scale;
+ * what happens past the range is this library's reading]. k_cache and v_cache are then written,
+ * so they must be writable memory although the signature declares them const. The matrix-core
+ * family writes the row inside the attention kernel; the other families run a small copy
+ * kernel first.
  *
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
  * opts is required (it carries kv_capacity). D in 1..256.

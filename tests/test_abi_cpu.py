@@ -36,9 +36,10 @@ def test_exports_every_declared_symbol(lib):
 def test_opts_layout_matches_header(lib):
     o = gqa.GqaOpts()
     lib.gqa_opts_init(ctypes.byref(o))
-    assert o.struct_size == ctypes.sizeof(gqa.GqaOpts) == 64
+    assert o.struct_size == ctypes.sizeof(gqa.GqaOpts) == 80
     assert (o.q_dtype, o.kv_dtype, o.kv_capacity, o.num_splits, o.path) == (1, 1, 0, 0, 0)
     assert not o.k_scale and not o.v_scale and not o.workspace and o.workspace_bytes == 0
+    assert not o.k_new and not o.v_new
 
 
 def test_status_strings():
@@ -91,6 +92,7 @@ INV, UNS, WSP = 1, 2, 3
     (dict(kv_dtype=2, k_scale=FAKE), INV),
     (dict(q_dtype=0, kv_dtype=0, D=3, path=3), UNS),   # matrix-core path needs bf16 q and D=128
     (dict(q_dtype=0, kv_dtype=0, D=3, path=2), UNS),   # vector path needs bf16 and D=128
+    (dict(k_new=FAKE), INV), (dict(v_new=FAKE), INV),  # cache append needs both rows
     (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), WSP),
     (dict(num_splits=4, workspace=FAKE + 4, workspace_bytes=1 << 30), INV),  # misaligned workspace
 ])
@@ -100,6 +102,17 @@ def test_decode_rejects(lib, kw, code):
 
 def test_decode_requires_opts(lib):
     assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, None) == INV
+
+
+def test_decode_short_struct_keeps_defaults(lib):
+    # A caller built against the layout without the append fields passes a shorter struct:
+    # the fields past struct_size are not read (here they hold an invalid lone k_new). The
+    # undersized workspace makes both calls fail on the host, at different checks.
+    o = gqa.new_opts(kv_capacity=64, k_new=FAKE, num_splits=4, workspace=FAKE, workspace_bytes=16)
+    o.struct_size = gqa.GqaOpts.k_new.offset
+    assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, ctypes.byref(o)) == WSP
+    o.struct_size = ctypes.sizeof(gqa.GqaOpts)
+    assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, ctypes.byref(o)) == INV
 
 
 def test_decode_short_struct(lib):
