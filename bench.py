@@ -6,7 +6,8 @@
 A step is one call of the hot path over one batch of synthetic inputs (seeded, from
 workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H32 G8
 D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
-B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown".
+B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown", and so are the headline
+and fp8 decodes with the current token's KV-cache append done by the same call ("+append").
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations. Each step reads the next of several replicas of its inputs, together
@@ -81,13 +82,17 @@ def measured_traffic(workload: str):
 # Algorithmic work per call (what the method must move / compute, nothing more).
 # ------------------------------------------------------------------------------------
 
-def decode_bytes(c: W.DecodeCase) -> dict:
-    """KV bytes = valid rows only: 2 (K and V) x sum_b L_b x G x D x element size."""
+def decode_bytes(c: W.DecodeCase, append: bool = False) -> dict:
+    """KV bytes = valid rows only: 2 (K and V) x sum_b L_b x G x D x element size. With a
+    cache append, the new K/V rows are read (q's dtype) and written (cache dtype) once more."""
     esz = {W.F32: 4, W.BF16: 2, W.FP8: 1}
     lens = c.seq_lens.clamp(0, c.T_cap).to(torch.int64)
     kv = 2 * int(lens.sum()) * c.G * c.D * esz[c.kv_dtype]
     qo = 2 * c.B * c.H * c.D * esz[c.q_dtype]
     extra = 4 * c.B + (8 * c.B * c.G if c.kv_dtype == W.FP8 else 0)   # seq_lens (+ fp8 scales)
+    if append:
+        n_rows = int(((c.seq_lens >= 1) & (c.seq_lens <= c.T_cap)).sum()) * c.G
+        extra += 2 * n_rows * c.D * (esz[c.q_dtype] + esz[c.kv_dtype])
     return {"kv": kv, "total": kv + qo + extra}
 
 
@@ -109,7 +114,7 @@ def prefill_bytes(c: W.PrefillCase) -> int:
 
 # ------------------------------------------------------------------------------------
 
-def make_decode_runner(gqa, c: W.DecodeCase, dev):
+def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
     kv_alloc = 2 * c.k_cache.numel() * c.k_cache.element_size()
     nrep = max(1, math.ceil(COLD_BYTES / kv_alloc))
     reps = []
@@ -123,11 +128,17 @@ def make_decode_runner(gqa, c: W.DecodeCase, dev):
     ws_bytes = gqa.decode_workspace_size(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     state = {"i": 0}
+    new = {}
+    if append:  # the current token's key and value, stored at row L-1 by the call itself
+        g = torch.Generator().manual_seed(1)
+        dt = c.q.dtype
+        new = {"k_new": torch.randn(c.B, c.G, c.D, generator=g).to(dt).to(dev),
+               "v_new": torch.randn(c.B, c.G, c.D, generator=g).to(dt).to(dev)}
 
     def step():
         q, k, v = reps[state["i"] % nrep]
         state["i"] += 1
-        gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws)
+        gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, **new)
 
     return step, nrep, out
 
@@ -210,23 +221,23 @@ def time_steps(step, steps, warmup, graph=True):
     return res
 
 
-def bench_decode(gqa, c, steps, warmup, dev):
-    step, nrep, _ = make_decode_runner(gqa, c, dev)
+def bench_decode(gqa, c, steps, warmup, dev, append=False):
+    step, nrep, _ = make_decode_runner(gqa, c, dev, append)
     t = time_steps(step, steps, warmup)
-    by = decode_bytes(c)
+    by = decode_bytes(c, append)
     s = t["ms_per_step"] * 1e-3
     launch = t["launch_ms_mean"] * 1e-3
     achieved = by["total"] / launch / 1e9
     return {
         "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T_cap": c.T_cap,
-        "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype,
+        "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype, "cache_append": append,
         "splits": gqa.decode_num_splits(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype),
         "kv_bytes": by["kv"], "algorithmic_bytes": by["total"], "flops": decode_flops(c),
         "kv_read_GBps": by["kv"] / s / 1e9, "tok_per_s": c.B / s,
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(c.name)},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None if append else measured_traffic(c.name)},
     }
 
 
@@ -307,14 +318,15 @@ def main():
     import grouped_query_attention_decode_amd as gqa
     gqa.library()
 
-    def run(name, steps, warmup):
+    def run(name, steps, warmup, append=False):
         case = W.WORKLOADS[name](0)
-        log(f"[bench] {name}: steps={steps} warmup={warmup}")
+        tag = name + ("+append" if append else "")
+        log(f"[bench] {tag}: steps={steps} warmup={warmup}")
         if isinstance(case, W.PrefillCase):
             r = bench_prefill(gqa, case, steps, warmup, dev)
         else:
-            r = bench_decode(gqa, case, steps, warmup, dev)
-        log(f"[bench] {name}: {json.dumps(r)}")
+            r = bench_decode(gqa, case, steps, warmup, dev, append)
+        log(f"[bench] {tag}: {json.dumps(r)}")
         return case, r
 
     case, head = run(args.workload, args.steps, args.warmup)
@@ -325,6 +337,11 @@ def main():
                 continue
             _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
             breakdown[name] = r
+        # The decode step with the current token's cache append done by the same call.
+        for name in dict.fromkeys((args.workload, "mqa_fp8_decode_B8_L32768")):
+            if W.WORKLOADS[name] is not W.causal_prefill_2048:
+                _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
+                breakdown[name + "+append"] = r
 
     is_prefill = isinstance(case, W.PrefillCase)
     cpu = None
