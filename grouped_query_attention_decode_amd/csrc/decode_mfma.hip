@@ -215,7 +215,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     }
 
     // One 32-token block: `slot` holds its K/V rows (requested earlier) and is refilled with
-    // the block `dist` rows ahead.
+    // the block `dist` rows ahead (dist = 0: the wave's last block, nothing to refill).
     auto step = [&](Frag<FP8> &slot, int t0, int dist) {
         Frag<FP8> cur = slot;
         // Rows at or past the end may hold anything, NaN included (a first block requested
@@ -247,12 +247,10 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                 *(i32x4_t *)(vt + r * RB + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
             }
         }
-        // Prefetch this slot's next block (dist rows ahead) before this block's work. The load is unconditional and
-        // branch-free (past the end it re-reads the current block, which the cache holds),
-        // and the barrier keeps the scheduler from sinking it next to its use -- otherwise
-        // every block waits out a full memory latency.
-        const int tn = t0 + dist < ke ? t0 + dist : t0;
-        load_block<FP8>(slot, kbase, vbase, tn, ke, lane);
+        // Prefetch this slot's next block (dist rows ahead, always inside the range) before this
+        // block's work; the barrier keeps the scheduler from sinking it next to its use --
+        // otherwise every block waits out a full memory latency.
+        if (dist > 0) load_block<FP8>(slot, kbase, vbase, t0 + dist, ke, lane);
         __builtin_amdgcn_sched_barrier(0);
 
         // S^T = K . Q^T for both 16-token sub-blocks and every head block.
@@ -349,7 +347,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
         for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep);
         if (po.append && tl + kBlockT >= ke) append_row<FP8>(nxt, a, bg, kbase, vbase, tl, ke - 1, lane);
-        step(nxt, tl, kStep);
+        step(nxt, tl, 0);
     }
 
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
@@ -400,15 +398,16 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             uint16_t *out = static_cast<uint16_t *>(a.out) + (head0 + h) * kD + d;
             *(i32x2_t *)out = i32x2_t{pack_bf16_rne(acc[0] * inv, acc[1] * inv), pack_bf16_rne(acc[2] * inv, acc[3] * inv)};
         } else {
-            float *pa = &a.part_acc[((head0 + h) * S + po.slot) * kD + d];
-            splitkv_store4(pa, f32x4_t{acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale},
-                           a.fuse_combine);
+            const f32x4_t v = {acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale};
+            if (a.fuse_combine)  // whole 16-byte chunks: every wave store writes full lines
+                splitkv_store4c(splitkv_acc_rsrc(a, head0, R), (unsigned)(((h * S + po.slot) * kD + d) * 4), v);
+            else
+                *(f32x4_t *)&a.part_acc[((head0 + h) * S + po.slot) * kD + d] = v;
             if (d == 0) {
                 float M = m_w[0][h];
 #pragma unroll
                 for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
-                splitkv_store(&a.part_ml[((head0 + h) * S + po.slot) * 2], M, a.fuse_combine);
-                splitkv_store(&a.part_ml[((head0 + h) * S + po.slot) * 2 + 1], l, a.fuse_combine);
+                splitkv_store_ml(&a.part_ml[((head0 + h) * S + po.slot) * 2], M, l, a.fuse_combine);
             }
         }
     }

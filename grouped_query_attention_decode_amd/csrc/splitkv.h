@@ -11,8 +11,9 @@
 // group's last range merges them itself instead of a second kernel. gfx950 gives every XCD
 // its own L2, and a device-scope release/acquire fence writes back and invalidates that whole
 // cache, which costs more than the merge saves. So the partials bypass the fences instead:
-// they are written and read with device-scope atomic stores and loads, which the hardware
-// keeps coherent across the L2s. Only the order of the operations remains to be enforced:
+// they are written and read with the cache policy of device-scope atomic stores and loads
+// (sc1; 16-byte buffer accesses for the accumulators), which the hardware keeps coherent
+// across the L2s. Only the order of the operations remains to be enforced:
 // every thread waits until its own partial stores have completed, the workgroup synchronises,
 // and one thread increments the group's arrival counter; the one that sees count = ranges - 1
 // merges in a fixed order (deterministic) and resets the counter to 0 for the next call. Its
@@ -44,17 +45,42 @@ __device__ __forceinline__ void splitkv_store(float *p, float v, int coherent) {
         *p = v;
 }
 
-__device__ __forceinline__ void splitkv_store4(float *p, f32x4_t v, int coherent) {
-    if (coherent) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) __hip_atomic_store(p + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        *(f32x4_t *)p = v;
-    }
-}
-
 __device__ __forceinline__ float splitkv_load(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// (m, l) of one range and query head as one 8-byte device-coherent store / load.
+__device__ __forceinline__ void splitkv_store_ml(float *p, float m, float l, int coherent) {
+    const unsigned long long bits = (unsigned long long)__float_as_uint(m) | ((unsigned long long)__float_as_uint(l) << 32);
+    if (coherent)
+        __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *reinterpret_cast<unsigned long long *>(p) = bits;
+}
+
+__device__ __forceinline__ f32x2_t splitkv_load_ml(const float *p) {
+    const unsigned long long bits =
+        __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x2_t{__uint_as_float((uint32_t)bits), __uint_as_float((uint32_t)(bits >> 32))};
+}
+
+// Buffer resource over the partial accumulators [R][S][D] of query heads head0 .. head0+R-1
+// (workgroup-uniform), for 16-byte device-coherent accesses: buffer loads and stores with the
+// cache-policy bit (sc1) that agent-scope atomic loads and stores carry. Offsets past the
+// resource's size read zero and write nothing instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t splitkv_acc_rsrc(const AttnArgs &a, long head0, int R) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(a.part_acc + head0 * a.num_splits * a.D), (short)0,
+                                             R * a.num_splits * a.D * 4, 0x00020000);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void splitkv_store4c(__amdgpu_buffer_rsrc_t r, unsigned byte_off, f32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, /*sc1*/ 16);
+}
+
+__device__ __forceinline__ f32x4_t splitkv_load4(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, /*sc1*/ 16));
 }
 
 // All threads call this after writing their partials with splitkv_store(.., 1). Returns, in
@@ -76,74 +102,91 @@ __device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active) {
 
 // Largest R * n_active a fused merge handles (the host checks R * S against it).
 constexpr int kMergeMaxPairs = 128;
-// Ranges whose accumulator loads one thread keeps in flight together.
-constexpr int kMergeBatch = 32;
 
-// out[h][d] = sum_s w[h][s] * acc_s[h][d] for the R heads of one group; each thread keeps
-// NB ranges' loads in flight at once.
+// Merge the n partials of query heads head0 .. head0+R-1 into out (bf16), using the whole
+// workgroup. part layout: acc [B*H][S][D], ml [B*H][S][2]; D is a multiple of 4. Every load
+// of another workgroup's partials travels to memory, and one compute unit completes only so
+// many of them at a time, so the accumulators are read 16 bytes per load and all loads are
+// issued before any is used: each (m, l) pair and up to NB ranges per thread at once, the
+// weights formed while the accumulators are in flight. A work item is 4 head dims of one
+// head; P = 1, 2 or 4 consecutive lanes share an item and take its ranges in turn, then add
+// their sums with lane shuffles. Ranges past n are not loaded into the sums (weight 0).
 template <int NB>
-__device__ __forceinline__ void splitkv_merge_rows(const AttnArgs &a, long head0, int R, int n, const float *w_s,
-                                                   uint16_t *out) {
-    const int S = a.num_splits, D = a.D;
-    for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-        const int h = e / D, d = e - (e / D) * D;
-        const float *acc = a.part_acc + (head0 + h) * S * D + d;
-        float num = 0.f;
-        for (int s0 = 0; s0 < n; s0 += NB) {
-            float x[NB];
+__device__ __forceinline__ void splitkv_merge_t(const AttnArgs &a, long head0, int R, int n, uint16_t *out) {
+    __shared__ float m_s[kMergeMaxPairs], l_s[kMergeMaxPairs], w_s[kMergeMaxPairs];
+    const int S = a.num_splits, D = a.D, t = threadIdx.x, nt = blockDim.x;
+    const int I = R * (D / 4);                                 // work items
+    const int P = 4 * I <= nt ? 4 : (2 * I <= nt ? 2 : 1);     // lanes per item
+    const __amdgpu_buffer_rsrc_t rsrc = splitkv_acc_rsrc(a, head0, R);
+    f32x2_t ml0 = {0.f, 0.f};
+    if (t < R * n) {
+        const int h = t / n, s = t - h * n;
+        ml0 = splitkv_load_ml(a.part_ml + ((head0 + h) * S + s) * 2);
+    }
+    const int p = t % P;
+    for (int i0 = 0; i0 < I; i0 += nt / P) {
+        const int item = min(i0 + t / P, I - 1);
+        const int h = item / (D / 4), d = 4 * (item - h * (D / 4));
+        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < n; s0 += NB * P) {
+            f32x4_t x[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int s = s0 + j < n ? s0 + j : n - 1;  // past the end: a valid, unused range
-                x[j] = splitkv_load(acc + (long)s * D);
+                const int sr = min(s0 + j * P + p, n - 1);
+                x[j] = splitkv_load4(rsrc, (unsigned)(((h * S + sr) * D + d) * 4));
+            }
+            if (i0 == 0 && s0 == 0) {
+                // Weight of pair t = (head h, range s): with M = max_s m_s and
+                // den = sum_s 2^(m_s - M) l_s of its head, w = 2^(m - M) / den. One thread per
+                // pair; every thread of a head forms M and den in the same order.
+                if (t < R * n) {
+                    m_s[t] = ml0[0];
+                    l_s[t] = ml0[1];
+                }
+                __syncthreads();
+                if (t < R * n) {
+                    // Unrolled so that the LDS reads go out eight at a time rather than one
+                    // round trip per range.
+                    const int hb = (t / n) * n;
+                    float M = -INFINITY;
+#pragma unroll 8
+                    for (int s = 0; s < n; ++s) M = fmaxf(M, m_s[hb + s]);
+                    float den = 0.f;
+#pragma unroll 8
+                    for (int s = 0; s < n; ++s) {
+                        const float m = m_s[hb + s], e = exp2f(m - M) * l_s[hb + s];
+                        den += m == -INFINITY ? 0.f : e;
+                    }
+                    w_s[t] = ml0[0] == -INFINITY || !(den > 0.f) ? 0.f : exp2f(ml0[0] - M) / den;
+                }
+                __syncthreads();
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const float w = s0 + j < n ? w_s[h * n + s0 + j] : 0.f;
-                num += w != 0.f ? w * x[j] : 0.f;
+                const int sr = s0 + j * P + p;
+                const float w = sr < n ? w_s[h * n + sr] : 0.f;
+                if (w != 0.f) {
+                    num[0] += w * x[j][0];
+                    num[1] += w * x[j][1];
+                    num[2] += w * x[j][2];
+                    num[3] += w * x[j][3];
+                }
             }
         }
-        out[(head0 + h) * D + d] = f32_to_bf16(num);
+        for (int o = 1; o < P; o <<= 1)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) num[c] += __shfl_xor(num[c], o);
+        if (p == 0 && i0 + t / P < I) {
+            uint16_t *dst = out + (head0 + h) * D + d;
+            *(i32x2_t *)dst = i32x2_t{(int)((uint32_t)f32_to_bf16(num[0]) | ((uint32_t)f32_to_bf16(num[1]) << 16)),
+                                      (int)((uint32_t)f32_to_bf16(num[2]) | ((uint32_t)f32_to_bf16(num[3]) << 16))};
+        }
     }
 }
 
-// Merge the n_active partials of query heads head0 .. head0+R-1 into out (bf16), using the
-// whole workgroup. part layout: acc [B*H][S][D], ml [B*H][S][2]. Every load of another
-// workgroup's partials is a device-coherent load and each costs a trip to memory, so they
-// are issued in batches: all (m, l) pairs at once, then up to 32 ranges per output element.
 __device__ __forceinline__ void splitkv_merge_bf16(const AttnArgs &a, long head0, int R, int n_active,
                                                    uint16_t *out) {
-    __shared__ float m_s[kMergeMaxPairs], w_s[kMergeMaxPairs];
-    const int S = a.num_splits, n = n_active;
-    for (int t = threadIdx.x; t < R * n; t += blockDim.x) {
-        const int h = t / n, s = t - h * n;
-        const float *ml = a.part_ml + ((head0 + h) * S + s) * 2;
-        m_s[t] = splitkv_load(ml);
-        w_s[t] = splitkv_load(ml + 1);
-    }
-    __syncthreads();
-    // Per head: M = max_s m_s, den = sum_s 2^(m_s - M) l_s; w_s becomes 2^(m_s - M) / den.
-    for (int h = threadIdx.x; h < R; h += blockDim.x) {
-        float M = -INFINITY;
-        for (int s = 0; s < n; ++s) M = fmaxf(M, m_s[h * n + s]);
-        float den = 0.f;
-        for (int s = 0; s < n; ++s) {
-            const float m = m_s[h * n + s];
-            const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-            den += w * w_s[h * n + s];
-            m_s[h * n + s] = w;
-        }
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        for (int s = 0; s < n; ++s) w_s[h * n + s] = m_s[h * n + s] * inv;
-    }
-    __syncthreads();
-    if (n <= 2)
-        splitkv_merge_rows<2>(a, head0, R, n, w_s, out);
-    else if (n <= 8)
-        splitkv_merge_rows<8>(a, head0, R, n, w_s, out);
-    else if (n <= 16)
-        splitkv_merge_rows<16>(a, head0, R, n, w_s, out);
-    else
-        splitkv_merge_rows<kMergeBatch>(a, head0, R, n, w_s, out);
+    splitkv_merge_t<8>(a, head0, R, n_active, out);
 }
 
 // ---- Flat layout of a ragged batch ----
