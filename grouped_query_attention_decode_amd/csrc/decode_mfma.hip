@@ -413,7 +413,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     }
     if (!po.direct && a.fuse_combine) {
         if (splitkv_arrive(a.counters + bg, po.n_slots))
-            splitkv_merge_bf16(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
+            splitkv_merge_bf16<kThreads, kD>(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
     }
 }
 

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(AttnArgs a) {
     }
     if (a.fuse_combine) {
         const int n_active = active_splits(L, a.split_len, S);
-        if (splitkv_arrive(a.counters + bg, n_active)) splitkv_merge_bf16(a, head0, R, n_active, out);
+        if (splitkv_arrive(a.counters + bg, n_active)) splitkv_merge_bf16<kThreads, kD>(a, head0, R, n_active, out);
     }
 }
 

@@ -104,20 +104,23 @@ __device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active) {
 constexpr int kMergeMaxPairs = 128;
 
 // Merge the n partials of query heads head0 .. head0+R-1 into out (bf16), using the whole
-// workgroup. part layout: acc [B*H][S][D], ml [B*H][S][2]; D is a multiple of 4. Every load
+// workgroup of NT threads. part layout: acc [B*H][S][D], ml [B*H][S][2]. Every load
 // of another workgroup's partials travels to memory, and one compute unit completes only so
 // many of them at a time, so the accumulators are read 16 bytes per load and all loads are
 // issued before any is used: each (m, l) pair and up to NB ranges per thread at once, the
 // weights formed while the accumulators are in flight. A work item is 4 head dims of one
 // head; P = 1, 2 or 4 consecutive lanes share an item and take its ranges in turn, then add
 // their sums with lane shuffles. Ranges past n are not loaded into the sums (weight 0).
-template <int NB>
+template <int NT, int D, int NB>
 __device__ __forceinline__ void splitkv_merge_t(const AttnArgs &a, long head0, int R, int n, uint16_t *out) {
+    static_assert(D % 4 == 0, "16-byte accumulator loads");
     __shared__ float m_s[kMergeMaxPairs], l_s[kMergeMaxPairs], w_s[kMergeMaxPairs];
-    const int S = a.num_splits, D = a.D, t = threadIdx.x, nt = blockDim.x;
+    constexpr int nt = NT;
+    const int S = a.num_splits, t = threadIdx.x;
     const int I = R * (D / 4);                                 // work items
     const int P = 4 * I <= nt ? 4 : (2 * I <= nt ? 2 : 1);     // lanes per item
-    const __amdgpu_buffer_rsrc_t rsrc = splitkv_acc_rsrc(a, head0, R);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(a.part_acc + head0 * S * D), (short)0,
+                                                                          R * S * D * 4, 0x00020000);
     f32x2_t ml0 = {0.f, 0.f};
     if (t < R * n) {
         const int h = t / n, s = t - h * n;
@@ -184,9 +187,12 @@ __device__ __forceinline__ void splitkv_merge_t(const AttnArgs &a, long head0, i
     }
 }
 
+// Merge for a workgroup of NT threads and head dim D (compile-time: no division by D and no
+// read of the launch's block size on the critical path).
+template <int NT, int D>
 __device__ __forceinline__ void splitkv_merge_bf16(const AttnArgs &a, long head0, int R, int n_active,
                                                    uint16_t *out) {
-    splitkv_merge_t<8>(a, head0, R, n_active, out);
+    splitkv_merge_t<NT, D, 8>(a, head0, R, n_active, out);
 }
 
 // ---- Flat layout of a ragged batch ----
