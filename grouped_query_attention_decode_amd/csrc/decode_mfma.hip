@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockT = 32;  // tokens per wave iteration
 constexpr int kD = 128;
+constexpr int kDP = kD + 4;  // row stride of the wave-merge tile: rows of 16 heads on distinct LDS banks
 
 // MFMA row m of token sub-block `blk` (0/1) holds token tau(blk, m) of the 32-token block,
 // so that C row 4*(l/16)+i of both sub-blocks lands in lane l as tokens 8*(l/16) + 4*blk + i.
@@ -353,7 +354,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
     // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
     // slice; every thread then sums four slices for 4 consecutive head dims.
-    float *o_w = reinterpret_cast<float *>(lds);  // [kWaves][HP][kD]
+    float *o_w = reinterpret_cast<float *>(lds);  // [kWaves][HP][kDP]
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -373,7 +374,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             if (h < R) {
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb)
-                    *(f32x4_t *)&o_w[(wave * HP + h) * kD + 16 * nb + 4 * (lane >> 4)] =
+                    *(f32x4_t *)&o_w[(wave * HP + h) * kDP + 16 * nb + 4 * (lane >> 4)] =
                         f32x4_t{o[hb][nb][0] * f, o[hb][nb][1] * f, o[hb][nb][2] * f, o[hb][nb][3] * f};
                 if (lane < 16) l_w[wave][h] = lsum[hb] * f;
             }
@@ -382,11 +383,11 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     __syncthreads();
     for (int cidx = threadIdx.x; cidx < R * (kD / 4); cidx += kThreads) {
         const int h = cidx / (kD / 4), d = 4 * (cidx % (kD / 4));
-        f32x4_t acc = *(const f32x4_t *)&o_w[h * kD + d];
+        f32x4_t acc = *(const f32x4_t *)&o_w[h * kDP + d];
         float l = l_w[0][h];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) {
-            const f32x4_t x = *(const f32x4_t *)&o_w[(w * HP + h) * kD + d];
+            const f32x4_t x = *(const f32x4_t *)&o_w[(w * HP + h) * kDP + d];
             acc[0] += x[0];
             acc[1] += x[1];
             acc[2] += x[2];
@@ -423,7 +424,7 @@ template <int NHB, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int HP = 16 * NHB;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kD * 4 ? kWaves * kBlockT * RB : kWaves * HP * kD * 4;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RB : kWaves * HP * kDP * 4;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
 
@@ -485,7 +486,7 @@ template <int NHB, bool FP8>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_kernel(AttnArgs a) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int HP = 16 * NHB;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kD * 4 ? kWaves * kBlockT * RB : kWaves * HP * kD * 4;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RB : kWaves * HP * kDP * 4;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
     __shared__ int lay_s[4];
