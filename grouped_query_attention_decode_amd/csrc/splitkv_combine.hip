@@ -98,13 +98,96 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(AttnArgs a) {
     if (threadIdx.x < D) store_f32(out, bh * D + d, den > 0.f ? num / den : 0.f);
 }
 
+// Head dims a multiple of 4: D threads per (sequence, query head). The four lanes of a quad
+// share head dims 4 (t / 4) .. +3 and take ranges s = t mod 4, +4, ..., eight per chunk of 32
+// ranges, with one 16-byte accumulator load and one 8-byte (m, l) load per range -- all of a
+// chunk's loads in flight at once; the quad then adds its sums with lane shuffles. Every quad
+// sees the same ranges, so the running maximum is the same in every lane. The first chunk is
+// requested before the flat layout's piece count is known (slots below S are allocated);
+// ranges at or past the count get weight 0 and their values are never used.
+template <typename QT, bool FLAT>
+__global__ __launch_bounds__(256) void splitkv_combine4_kernel(AttnArgs a) {
+    const int S = a.num_splits, D = a.D;
+    const long bh = blockIdx.x;
+    const int t = threadIdx.x, p = t & 3, d = 4 * (t >> 2);
+    const float *ml = a.part_ml + bh * S * 2;
+    const float *acc = a.part_acc + bh * S * D + d;
+    f32x4_t x[8];
+    f32x2_t mlv[8];
+    auto load_chunk = [&](int s0, int lim) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = min(s0 + 4 * j + p, lim - 1);
+            x[j] = *(const f32x4_t *)(acc + (long)s * D);
+            mlv[j] = *(const f32x2_t *)(ml + 2 * s);
+        }
+    };
+    load_chunk(0, S);
+    int n = S;
+    if constexpr (FLAT) {
+        const int b = (int)(bh / a.H), g = (int)(bh % a.H) / (a.H / a.G);
+        n = flat_row_pieces(a, b, g);
+        if (n == 1) return;
+    }
+    float M = -INFINITY, den = 0.f;
+    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n; s0 += 32) {
+        if (s0 > 0) load_chunk(s0, n);
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + 4 * j + p < n) Mc = fmaxf(Mc, mlv[j][0]);
+        Mc = fmaxf(Mc, __shfl_xor(Mc, 1));
+        Mc = fmaxf(Mc, __shfl_xor(Mc, 2));
+        if (Mc == -INFINITY) continue;  // no keys in any range so far
+        const float alpha = M == -INFINITY ? 0.f : exp2f(M - Mc);
+        den *= alpha;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[c] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float m = mlv[j][0];
+            const float w = (s0 + 4 * j + p < n && m != -INFINITY) ? exp2f(m - Mc) : 0.f;
+            if (w != 0.f) {  // never 0 * (unwritten value)
+                den += w * mlv[j][1];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) num[c] += w * x[j][c];
+            }
+        }
+        M = Mc;
+    }
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+        den += __shfl_xor(den, o);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[c] += __shfl_xor(num[c], o);
+    }
+    if (p == 0) {
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) store_f32(static_cast<QT *>(a.out), bh * D + d + c, den > 0.f ? num[c] * inv : 0.f);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const AttnArgs &a, hipStream_t stream) {
     if (a.D > 256) return hipErrorInvalidValue;
-    dim3 grid((unsigned)(a.B * a.H));
-    dim3 block((unsigned)((a.D + 63) / 64 * 64));
-    if (a.q_dtype == DT_F32) {
+    const dim3 grid((unsigned)(a.B * a.H));
+    const bool f32 = a.q_dtype == DT_F32;
+    if (a.D % 4 == 0) {
+        const dim3 block((unsigned)a.D);
+        if (f32) {
+            if (a.flat) hipLaunchKernelGGL((splitkv_combine4_kernel<float, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((splitkv_combine4_kernel<float, false>), grid, block, 0, stream, a);
+        } else {
+            if (a.flat) hipLaunchKernelGGL((splitkv_combine4_kernel<uint16_t, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((splitkv_combine4_kernel<uint16_t, false>), grid, block, 0, stream, a);
+        }
+        return hipGetLastError();
+    }
+    const dim3 block((unsigned)((a.D + 63) / 64 * 64));
+    if (f32) {
         if (a.flat) hipLaunchKernelGGL((splitkv_combine_kernel<float, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((splitkv_combine_kernel<float, false>), grid, block, 0, stream, a);
     } else {
