@@ -7,7 +7,8 @@ A step is one call of the hot path over one batch of synthetic inputs (seeded, f
 workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H32 G8
 D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
 B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown", and so are the headline
-and fp8 decodes with the current token's KV-cache append done by the same call ("+append").
+and fp8 decodes with the current token's KV-cache append done by the same call ("+append"),
+and three decodes over a cache in shuffled 16-row pages ("_paged16").
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations. Each step reads the next of several replicas of its inputs, together
@@ -93,6 +94,8 @@ def decode_bytes(c: W.DecodeCase, append: bool = False) -> dict:
     if append:
         n_rows = int(((c.seq_lens >= 1) & (c.seq_lens <= c.T_cap)).sum()) * c.G
         extra += 2 * n_rows * c.D * (esz[c.q_dtype] + esz[c.kv_dtype])
+    if isinstance(c, W.PagedDecodeCase):  # block-table entries of the pages holding valid rows
+        extra += 4 * int(((lens + c.page_size - 1) // c.page_size).sum())
     return {"kv": kv, "total": kv + qo + extra}
 
 
@@ -115,10 +118,12 @@ def prefill_bytes(c: W.PrefillCase) -> int:
 # ------------------------------------------------------------------------------------
 
 def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
-    kv_alloc = 2 * c.k_cache.numel() * c.k_cache.element_size()
+    paged = isinstance(c, W.PagedDecodeCase)
+    kk, vv = (c.k_pages, c.v_pages) if paged else (c.k_cache, c.v_cache)
+    kv_alloc = 2 * kk.numel() * kk.element_size()
     nrep = max(1, math.ceil(COLD_BYTES / kv_alloc))
     reps = []
-    base = [c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)]
+    base = [c.q.to(dev), kk.to(dev), vv.to(dev)]
     for i in range(nrep):
         reps.append(base if i == 0 else [t.clone() for t in base])
     lens = c.seq_lens.to(dev)
@@ -135,10 +140,16 @@ def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
         new = {"k_new": torch.randn(c.B, c.G, c.D, generator=g).to(dt).to(dev),
                "v_new": torch.randn(c.B, c.G, c.D, generator=g).to(dt).to(dev)}
 
+    table = c.block_table.to(dev) if paged else None
+
     def step():
         q, k, v = reps[state["i"] % nrep]
         state["i"] += 1
-        gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, **new)
+        if paged:
+            gqa.decode_paged(q, k, v, table, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws,
+                             **new)
+        else:
+            gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, **new)
 
     return step, nrep, out
 
@@ -231,13 +242,15 @@ def bench_decode(gqa, c, steps, warmup, dev, append=False):
     return {
         "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T_cap": c.T_cap,
         "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype, "cache_append": append,
+        "page_size": c.page_size if isinstance(c, W.PagedDecodeCase) else None,
         "splits": gqa.decode_num_splits(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype),
         "kv_bytes": by["kv"], "algorithmic_bytes": by["total"], "flops": decode_flops(c),
         "kv_read_GBps": by["kv"] / s / 1e9, "tok_per_s": c.B / s,
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None if append else measured_traffic(c.name)},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if append or isinstance(c, W.PagedDecodeCase) else measured_traffic(c.name)},
     }
 
 
@@ -342,6 +355,13 @@ def main():
             if W.WORKLOADS[name] is not W.causal_prefill_2048:
                 _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
                 breakdown[name + "+append"] = r
+        # The same decodes over a cache in shuffled pages of 16 rows.
+        for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
+            pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)
+            log(f"[bench] {pc.name}")
+            r = bench_decode(gqa, pc, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
+            log(f"[bench] {pc.name}: {json.dumps(r)}")
+            breakdown[pc.name] = r
 
     is_prefill = isinstance(case, W.PrefillCase)
     cpu = None

@@ -6,6 +6,8 @@ the current stream. There is no fallback: if the library is not built, or the de
 not gfx950, calls raise.
 
     decode(q, k_cache, v_cache, seq_lens, ...)   q [B,H,D], caches [B,G,T_cap,D]
+    decode_paged(q, k_pages, v_pages, block_table, seq_lens, ...)
+                                                 pools [num_pages,G,page_size,D], table [B,pages_per_seq]
     prefill(q, k, v, causal=True, ...)           q [B,H,T,D], k/v [B,G,T,D]
 """
 
@@ -17,7 +19,7 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
-__all__ = ["decode", "prefill", "decode_num_splits", "decode_workspace_size", "status_string",
+__all__ = ["decode", "decode_paged", "prefill", "decode_num_splits", "decode_workspace_size", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
@@ -84,6 +86,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_opts_init.restype = None
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_decode.restype = i
+    lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_decode_paged.restype = i
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_prefill.restype = i
     lib.gqa_decode_num_splits.argtypes = [i] * 7
@@ -144,6 +148,34 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream)
 
 
+def _decode_opts(q, cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, layout, k_new, v_new, workspace):
+    kv_code = _dtype_code(cache, "k_cache")
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
+                 num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
+    if kv_code == DTYPES["fp8_e4m3fn"]:
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 caches need k_scale and v_scale")
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need_cuda(t, n)
+            if t.dtype != torch.float32 or t.numel() != B * G:
+                raise ValueError(f"{n} must be float32 [B*G]")
+        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _need_cuda(t, n)
+            if t.dtype != q.dtype or tuple(t.shape) != (B, G, D):
+                raise ValueError(f"{n} must be [B, G, D] = {(B, G, D)} in q's dtype")
+        o.k_new, o.v_new = k_new.data_ptr(), v_new.data_ptr()
+    need = decode_workspace_size(B, q.shape[1], G, D, T_cap, kv_code, int(num_splits))
+    if need > 0:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        o.workspace, o.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return o, workspace
+
+
 def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
            num_splits=0, path="auto", workspace=None, stream=None, layout="auto", k_new=None, v_new=None):
     """Single-token GQA decode. Returns ``out`` [B, H, D] (q's dtype).
@@ -173,35 +205,49 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
     _need_cuda(out, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    kv_code = _dtype_code(k_cache, "k_cache")
-    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
-                 num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
-    if kv_code == DTYPES["fp8_e4m3fn"]:
-        if k_scale is None or v_scale is None:
-            raise ValueError("fp8 caches need k_scale and v_scale")
-        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
-            _need_cuda(t, n)
-            if t.dtype != torch.float32 or t.numel() != B * G:
-                raise ValueError(f"{n} must be float32 [B*G]")
-        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
-    if (k_new is None) != (v_new is None):
-        raise ValueError("k_new and v_new go together")
-    if k_new is not None:
-        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-            _need_cuda(t, n)
-            if t.dtype != q.dtype or tuple(t.shape) != (B, G, D):
-                raise ValueError(f"{n} must be [B, G, D] = {(B, G, D)} in q's dtype")
-        o.k_new, o.v_new = k_new.data_ptr(), v_new.data_ptr()
-    need = decode_workspace_size(B, H, G, D, T_cap, kv_code, int(num_splits))
-    if need > 0:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-        o.workspace, o.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    o, workspace = _decode_opts(q, k_cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, layout,
+                                k_new, v_new, workspace)
     st = library().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                               out.data_ptr(), B, H, G, D, float(scale), _stream_handle(stream, q.device),
                               ctypes.byref(o))
     if st != GQA_OK:
         raise GqaError(st, "gqa_decode")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=None, k_scale=None, v_scale=None,
+                 num_splits=0, path="auto", workspace=None, stream=None, layout="auto", k_new=None, v_new=None):
+    """Single-token GQA decode over a paged cache. Returns ``out`` [B, H, D] (q's dtype).
+
+    ``k_pages``/``v_pages`` [num_pages, G, page_size, D]; ``block_table`` int32 [B, pages_per_seq]:
+    row t of sequence b is row t % page_size of page block_table[b, t // page_size]. The other
+    arguments are those of ``decode`` (the workspace size is that of a cache of
+    pages_per_seq * page_size rows)."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens")):
+        _need_cuda(t, n)
+    if q.dim() != 3 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B,H,D], pools [num_pages,G,page_size,D] and block_table [B,pages_per_seq]")
+    B, H, D = q.shape
+    num_pages, G, page_size, Dk = k_pages.shape
+    Bt, pages_per_seq = block_table.shape
+    if Bt != B or Dk != D or block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, pools, block_table (int32) and seq_lens (int32 [B])")
+    if k_pages.dtype != v_pages.dtype:
+        raise TypeError("k_pages and v_pages must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o, workspace = _decode_opts(q, k_pages, B, G, D, pages_per_seq * page_size, k_scale, v_scale, num_splits,
+                                path, layout, k_new, v_new, workspace)
+    st = library().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                    seq_lens.data_ptr(), out.data_ptr(), B, H, G, D, float(scale), page_size,
+                                    pages_per_seq, num_pages, _stream_handle(stream, q.device), ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_decode_paged")
     return out
 
 

@@ -58,23 +58,67 @@ template <bool FP8> struct Frag;
 template <> struct Frag<false> { i32x4_t k[8]; i32x4_t v[8]; };
 template <> struct Frag<true> { i32x4_t k[4]; i32x4_t v[4]; };
 
-template <bool FP8>
-__device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, const char *vbase, int t0, int ke,
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+
+// Where the key/value rows of one (sequence, KV head) live. Contiguous: k, v point at row 0
+// of the slab. Paged: k, v point at the page pools advanced to KV head g (a page holds the
+// 2^ps_log2 rows of all G heads, page_bytes long) and bt at the sequence's block-table row,
+// read through the scalar cache (the table is not written during a launch).
+struct KvSrc {
+    const char *k, *v;
+    long page_bytes;
+    cint32_t *bt;
+    int ps_log2, n_bt, num_pages;
+};
+
+// Pool offsets of the (at most three) pages that rows t0 .. t0+31 fall in; pages have at
+// least 16 rows. Table positions past the row and page ids outside the pool are clamped, so
+// every address stays inside the allocations whatever the table holds.
+struct PageOffs {
+    long o0, o1, o2;  // separate fields: an array here was indexed through scratch memory
+};
+
+template <bool PAGED>
+__device__ __forceinline__ PageOffs fetch_pages(const KvSrc &s, int t0) {
+    PageOffs p = {};
+    if constexpr (PAGED) {
+        const int p0 = t0 >> s.ps_log2;
+        auto off = [&](int k) { return (long)min(max(s.bt[min(p0 + k, s.n_bt - 1)], 0), s.num_pages - 1) * s.page_bytes; };
+        p.o0 = off(0);
+        p.o1 = off(1);
+        p.o2 = off(2);
+    }
+    return p;
+}
+
+// Byte offset of row r (t0 <= r < t0 + 32) from k / v.
+template <bool PAGED, int RB>
+__device__ __forceinline__ long row_off(const KvSrc &s, PageOffs p, int t0, int r) {
+    if constexpr (PAGED) {
+        const int rel = (r >> s.ps_log2) - (t0 >> s.ps_log2);
+        const long base = rel == 0 ? p.o0 : (rel == 1 ? p.o1 : p.o2);
+        return base + (long)(r & ((1 << s.ps_log2) - 1)) * RB;
+    } else {
+        return (long)r * RB;
+    }
+}
+
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void load_block(Frag<FP8> &f, const KvSrc &src, PageOffs pg, int t0, int ke,
                                            int lane) {
     constexpr int RB = FP8 ? 128 : 256;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         int row = t0 + tau(blk, lane & 15);
         row = row < ke ? row : ke - 1;
+        const char *kr = src.k + row_off<PAGED, RB>(src, pg, t0, row);
         if constexpr (FP8) {
             // 16 fp8 per lane: head dims 64p + 16*(l/16) .. +15 feed k-steps 2p and 2p+1.
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                f.k[blk * 2 + p] = *(const i32x4_t *)(kbase + (long)row * RB + 64 * p + 16 * (lane >> 4));
+            for (int p = 0; p < 2; ++p) f.k[blk * 2 + p] = *(const i32x4_t *)(kr + 64 * p + 16 * (lane >> 4));
         } else {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                f.k[blk * 4 + kk] = *(const i32x4_t *)(kbase + (long)row * RB + 64 * kk + 16 * (lane >> 4));
+            for (int kk = 0; kk < 4; ++kk) f.k[blk * 4 + kk] = *(const i32x4_t *)(kr + 64 * kk + 16 * (lane >> 4));
         }
     }
     if constexpr (FP8) {
@@ -82,14 +126,14 @@ __device__ __forceinline__ void load_block(Frag<FP8> &f, const char *kbase, cons
         for (int i = 0; i < 4; ++i) {
             int row = t0 + 8 * i + (lane >> 3);
             row = row < ke ? row : ke - 1;
-            f.v[i] = *(const i32x4_t *)(vbase + (long)row * RB + 16 * (lane & 7));
+            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 7));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             int row = t0 + 4 * i + (lane >> 4);
             row = row < ke ? row : ke - 1;
-            f.v[i] = *(const i32x4_t *)(vbase + (long)row * RB + 16 * (lane & 15));
+            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 15));
         }
     }
 }
@@ -117,14 +161,15 @@ __device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp
 // operand layout and in the V row layout alike -- put the new chunk (quantised for an fp8
 // cache) in its place and store it to the cache, so the row is written once and attended to
 // with exactly the bytes stored.
-template <bool FP8>
-__device__ __forceinline__ void append_row(Frag<FP8> &f, const AttnArgs &a, int bg, const char *kbase,
-                                           const char *vbase, int t0, int r, int lane) {
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void append_row(Frag<FP8> &f, const AttnArgs &a, int bg, const KvSrc &src, int t0, int r,
+                                           int lane) {
     constexpr int RB = FP8 ? 128 : 256;
     const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (long)bg * kD;
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (long)bg * kD;
-    char *kr = const_cast<char *>(kbase) + (long)r * RB;
-    char *vr = const_cast<char *>(vbase) + (long)r * RB;
+    const long ro = row_off<PAGED, RB>(src, fetch_pages<PAGED>(src, t0), t0, r);
+    char *kr = const_cast<char *>(src.k) + ro;
+    char *vr = const_cast<char *>(src.v) + ro;
     const int rb = r - t0;  // row in the block, 0..31
     // Registers are chosen by per-lane predicates over compile-time indices, so that the
     // fragment stays in registers.
@@ -189,11 +234,11 @@ struct PieceOut {
 // Attention of query heads head0 .. head0+R-1 over key rows kb .. ke-1 of one (sequence, KV
 // head), by the whole workgroup: each wave streams blocks kb + 32 (wave + 4 i), then the four
 // waves merge. The caller has requested q (qT) and this wave's first block (nxt) already.
-template <int NHB, bool FP8>
+template <int NHB, bool FP8, bool PAGED>
 __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w)[16 * NHB], float (*l_w)[16 * NHB],
                                        int lane, int wave, long head0, int R, int bg, int kb, int ke, PieceOut po,
-                                       i32x4_t (&qT)[NHB][4], Frag<FP8> &nxt, const char *kbase,
-                                       const char *vbase, float c, float vscale) {
+                                       i32x4_t (&qT)[NHB][4], Frag<FP8> &nxt, const KvSrc &src, float c,
+                                       float vscale) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int VT = kBlockT * RB;  // V tile bytes per wave
     constexpr int HP = 16 * NHB;      // heads padded to MFMA blocks
@@ -214,6 +259,11 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) o[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+
+    constexpr int kStep = kWaves * kBlockT;
+    // Paged: pool offsets of the pages of the block to prefetch next (the wave's second block);
+    // page ids are requested one block before the rows they locate.
+    PageOffs pgn = fetch_pages<PAGED>(src, kb + wave * kBlockT + kStep);
 
     // One 32-token block: `slot` holds its K/V rows (requested earlier) and is refilled with
     // the block `dist` rows ahead (dist = 0: the wave's last block, nothing to refill).
@@ -251,7 +301,10 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         // Prefetch this slot's next block (dist rows ahead, always inside the range) before this
         // block's work; the barrier keeps the scheduler from sinking it next to its use --
         // otherwise every block waits out a full memory latency.
-        if (dist > 0) load_block<FP8>(slot, kbase, vbase, t0 + dist, ke, lane);
+        if (dist > 0) {
+            load_block<FP8, PAGED>(slot, src, pgn, t0 + dist, ke, lane);
+            if constexpr (PAGED) pgn = fetch_pages<PAGED>(src, t0 + 2 * dist);  // for the next prefetch
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // S^T = K . Q^T for both 16-token sub-blocks and every head block.
@@ -340,14 +393,13 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             for (int hb = 0; hb < NHB; ++hb) o[hb][nb] = mfma16x16x32(va, pb[hb], o[hb][nb]);
         }
         };
-    constexpr int kStep = kWaves * kBlockT;
     int t0 = kb + wave * kBlockT;
     if (t0 < ke) {
         // The wave's last block is peeled off the loop: it is the one that may hold the row
         // of a cache append, and code for that kept out of the loop costs it no registers.
         const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
         for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep);
-        if (po.append && tl + kBlockT >= ke) append_row<FP8>(nxt, a, bg, kbase, vbase, tl, ke - 1, lane);
+        if (po.append && tl + kBlockT >= ke) append_row<FP8, PAGED>(nxt, a, bg, src, tl, ke - 1, lane);
         step(nxt, tl, 0);
     }
 
@@ -418,9 +470,30 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     }
 }
 
+// The rows of (sequence b, KV head g): a slab of the contiguous cache, or the page pools and
+// the sequence's block-table row.
+template <bool PAGED, int RB>
+__device__ __forceinline__ KvSrc kv_src(const AttnArgs &a, int b, int g, int bg) {
+    KvSrc s = {};
+    if constexpr (PAGED) {
+        const long ps_bytes = (long)RB << a.ps_log2;
+        s.k = static_cast<const char *>(a.k) + g * ps_bytes;
+        s.v = static_cast<const char *>(a.v) + g * ps_bytes;
+        s.page_bytes = a.G * ps_bytes;
+        s.bt = (cint32_t *)(a.block_table + (long)b * a.pages_per_seq);
+        s.ps_log2 = a.ps_log2;
+        s.n_bt = a.pages_per_seq;
+        s.num_pages = a.num_pages;
+    } else {
+        s.k = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
+        s.v = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+    }
+    return s;
+}
+
 // Uniform layout: workgroup = (key range `split`, sequence b, KV head g), ranges of split_len
 // keys. Split-major order: the blocks resident on one CU at once are far apart in the grid.
-template <int NHB, bool FP8>
+template <int NHB, bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int HP = 16 * NHB;
@@ -446,10 +519,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
     const float kscale = FP8 ? a.k_scale[bg] : 1.f;
     const float vscale = FP8 ? a.v_scale[bg] : 1.f;
-    const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
-    const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+    const KvSrc src = kv_src<PAGED, RB>(a, b, g, bg);
     Frag<FP8> nxt;
-    if (kb + wave * kBlockT < a.Tk) load_block<FP8>(nxt, kbase, vbase, kb + wave * kBlockT, a.Tk, lane);
+    if (kb + wave * kBlockT < a.Tk)
+        load_block<FP8, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, a.Tk, lane);
 
     const int Lraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     const int L = clamp_len(Lraw, a.Tk);
@@ -475,14 +548,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     // With the in-kernel merge, a sequence whose keys all fall in this range needs no merge.
     po.direct = S == 1 || (a.fuse_combine && po.n_slots == 1);
     po.append = a.k_new && ke == L && Lraw == L;  // Lraw in 1..T_cap: the row exists
-    attend<NHB, FP8>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, kbase, vbase,
-                     a.scale_log2 * kscale, vscale);
+    attend<NHB, FP8, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
+                            a.scale_log2 * kscale, vscale);
 }
 
 // Flat layout (splitkv.h): workgroup w streams rows [w C, (w + 1) C) of the concatenated
 // segments, piece by piece. Every workgroup gets the same number of rows, whatever the mix of
 // sequence lengths.
-template <int NHB, bool FP8>
+template <int NHB, bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_kernel(AttnArgs a) {
     constexpr int RB = FP8 ? 128 : 256;
     constexpr int HP = 16 * NHB;
@@ -564,34 +637,35 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_k
         load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
         const float kscale = FP8 ? a.k_scale[bg] : 1.f;
         const float vscale = FP8 ? a.v_scale[bg] : 1.f;
-        const char *kbase = static_cast<const char *>(a.k) + (long)bg * a.Tk * RB;
-        const char *vbase = static_cast<const char *>(a.v) + (long)bg * a.Tk * RB;
+        const KvSrc src = kv_src<PAGED, RB>(a, b, g, bg);
         Frag<FP8> nxt;
-        if (kb + wave * kBlockT < ke) load_block<FP8>(nxt, kbase, vbase, kb + wave * kBlockT, ke, lane);
-        attend<NHB, FP8>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, kbase, vbase,
+        if (kb + wave * kBlockT < ke)
+            load_block<FP8, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, ke, lane);
+        attend<NHB, FP8, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
                          a.scale_log2 * kscale, vscale);
         __syncthreads();  // the next piece reuses the LDS tiles
         x = s0 + ke;
     }
 }
 
-template <int NHB, bool FP8>
+template <int NHB, bool FP8, bool PAGED>
 hipError_t launch_nhb(const AttnArgs &a, hipStream_t stream) {
     if (a.flat) {
-        hipLaunchKernelGGL((decode_mfma_flat_kernel<NHB, FP8>), dim3((unsigned)a.flat_nw), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_flat_kernel<NHB, FP8, PAGED>), dim3((unsigned)a.flat_nw), dim3(kThreads), 0,
+                           stream, a);
     } else {
         dim3 grid((unsigned)(a.B * a.G * a.num_splits));
-        hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8, PAGED>), grid, dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
 
-template <bool FP8>
+template <bool FP8, bool PAGED>
 hipError_t launch_kv(const AttnArgs &a, hipStream_t stream) {
     const int R = a.H / a.G;
-    if (R <= 16) return launch_nhb<1, FP8>(a, stream);
-    if (R <= 32) return launch_nhb<2, FP8>(a, stream);
-    return launch_nhb<4, FP8>(a, stream);
+    if (R <= 16) return launch_nhb<1, FP8, PAGED>(a, stream);
+    if (R <= 32) return launch_nhb<2, FP8, PAGED>(a, stream);
+    return launch_nhb<4, FP8, PAGED>(a, stream);
 }
 
 }  // namespace
@@ -603,7 +677,9 @@ bool decode_mfma_supports(const AttnArgs &a) {
 
 hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream) {
     if (!decode_mfma_supports(a)) return hipErrorInvalidValue;
-    return a.kv_dtype == DT_FP8 ? launch_kv<true>(a, stream) : launch_kv<false>(a, stream);
+    if (a.block_table)
+        return a.kv_dtype == DT_FP8 ? launch_kv<true, true>(a, stream) : launch_kv<false, true>(a, stream);
+    return a.kv_dtype == DT_FP8 ? launch_kv<true, false>(a, stream) : launch_kv<false, false>(a, stream);
 }
 
 }  // namespace gqa

@@ -230,13 +230,35 @@ size_t gqa_decode_workspace_size(int B, int H, int G, int D, int kv_capacity, in
     return workspace_bytes_for(B, H, G, D, S);
 }
 
-gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
-                      void *out, int B, int H, int G, int D, float scale, hipStream_t stream,
-                      const gqa_opts *opts_in) {
+}  // extern "C"
+
+namespace gqa {
+namespace {
+
+// Paged cache geometry (null for the contiguous cache).
+struct PagedDesc {
+    const int32_t *block_table;
+    int page_size, pages_per_seq, num_pages;
+};
+
+gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *out,
+                       int B, int H, int G, int D, float scale, hipStream_t stream, const gqa_opts *opts_in,
+                       const PagedDesc *pg) {
     // ---- host-side validation (no HIP calls) ----
     if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
     gqa_opts o;
     if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
+    int ps_log2 = 0;
+    if (pg) {
+        // Rows per page: a power of two from 16 (a 32-row block then spans at most three
+        // pages) to 2^20; the capacity replaces opts->kv_capacity.
+        if (!pg->block_table || pg->pages_per_seq < 1 || pg->num_pages < 1) return GQA_ERR_INVALID_ARG;
+        if (pg->page_size < 16 || pg->page_size > (1 << 20) || (pg->page_size & (pg->page_size - 1)) != 0)
+            return GQA_ERR_INVALID_ARG;
+        while ((1 << ps_log2) < pg->page_size) ++ps_log2;
+        if ((long)pg->pages_per_seq * pg->page_size > 0x7fffffffL) return GQA_ERR_INVALID_ARG;
+        o.kv_capacity = pg->pages_per_seq * pg->page_size;
+    }
     if (o.layout < GQA_LAYOUT_AUTO || o.layout > GQA_LAYOUT_FLAT) return GQA_ERR_INVALID_ARG;
     if (o.layout == GQA_LAYOUT_FLAT && o.num_splits > 0) return GQA_ERR_INVALID_ARG;
     if (!decode_sizes_ok(B, H, G, D, o.kv_capacity)) return GQA_ERR_INVALID_ARG;
@@ -261,8 +283,15 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     a.causal = 0; a.decode = 1;
     a.scale_log2 = scale * kLog2e;
     a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
+    if (pg) {
+        a.block_table = pg->block_table;
+        a.ps_log2 = ps_log2;
+        a.pages_per_seq = pg->pages_per_seq;
+        a.num_pages = pg->num_pages;
+    }
     int path = o.path;
     if (path == GQA_PATH_AUTO) path = decode_mfma_supports(a) ? GQA_PATH_MFMA : GQA_PATH_GENERIC;
+    if (pg && path != GQA_PATH_MFMA) return GQA_ERR_UNSUPPORTED;  // paged: matrix-core family only
     if (path == GQA_PATH_VALU && !decode_valu_supports(a)) return GQA_ERR_UNSUPPORTED;
     if (path == GQA_PATH_MFMA && !decode_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
 
@@ -325,6 +354,25 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
         if (e == hipSuccess) e = f;
     }
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace gqa
+
+extern "C" {
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                      void *out, int B, int H, int G, int D, float scale, hipStream_t stream,
+                      const gqa_opts *opts) {
+    return gqa::decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, G, D, scale, stream, opts, nullptr);
+}
+
+gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                            const int32_t *seq_lens, void *out, int B, int H, int G, int D, float scale,
+                            int page_size, int pages_per_seq, int num_pages, hipStream_t stream,
+                            const gqa_opts *opts) {
+    const gqa::PagedDesc pg = {block_table, page_size, pages_per_seq, num_pages};
+    return gqa::decode_impl(q, k_pages, v_pages, seq_lens, out, B, H, G, D, scale, stream, opts, &pg);
 }
 
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, int B, int T, int H, int G,

@@ -11,8 +11,8 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 // Everything one attention launch needs. Pointers are device pointers.
 struct AttnArgs {
     const void *q;            // decode [B,H,D]; prefill [B,H,T,D]
-    const void *k;            // decode [B,G,T_cap,D]; prefill [B,G,T,D]
-    const void *v;
+    const void *k;            // decode [B,G,T_cap,D], or paged [num_pages][G][page_size][D];
+    const void *v;            //   prefill [B,G,T,D]
     void *out;                // same shape and type as q
     const int32_t *seq_lens;  // decode only
     const float *k_scale;     // fp8 only, [B*G]
@@ -21,6 +21,10 @@ struct AttnArgs {
     float *part_ml;           // split partials, [B*H][S][2] = (running max, running sum)
     const void *k_new;        // decode with append: the current token's key [B*G][D] (q's dtype)
     const void *v_new;        //   and value; both null without append
+    const int32_t *block_table;  // paged decode: [B][pages_per_seq] page ids, else null
+    int ps_log2;              // paged decode: log2(rows per page)
+    int pages_per_seq;        // paged decode: block-table row length (T_cap = pages_per_seq << ps_log2)
+    int num_pages;            // paged decode: pages in each pool
     int *counters;            // split arrival counters, [B*G], zero between calls
     int fuse_combine;         // 1: the last workgroup of each (b, g) merges the partials
     int B, H, G, D;

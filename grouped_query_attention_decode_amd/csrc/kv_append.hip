@@ -1,5 +1,6 @@
 // Cache append as its own kernel, for the decode families that do not fuse it (generic and
-// vector-ALU): the current token's key and value, [B*G][D] in q's dtype, are stored at row
+// vector-ALU) and for new rows that are not 16-byte aligned: the current token's key and
+// value, [B*G][D] in q's dtype, are stored at (logical) row
 // L_b - 1 of every (b, g) with 1 <= L_b <= T_cap ("LLM principles -- code implementation of
 // multi-head attention (MQA and GQA)", sections 3 and 5: the new K/V are appended to the
 // cache before the scores). fp32 and bf16 caches take the values unchanged; fp8 caches take
@@ -16,11 +17,20 @@ namespace {
 template <typename QT, typename KT, bool FP8>
 __global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a) {
     const int bg = blockIdx.x;
-    const int b = bg / a.G;
+    const int b = bg / a.G, g = bg - b * a.G;
     const int L = a.seq_lens[b];
     const int d = threadIdx.x;
     if (L < 1 || L > a.Tk || d >= a.D) return;
-    const long i = ((long)bg * a.Tk + (L - 1)) * a.D + d;
+    long i;  // element index of row L-1, head dim d
+    if (a.block_table) {
+        // Paged cache [num_pages][G][page_size][D]; page ids outside the pool are clamped.
+        const int r = L - 1, ps = 1 << a.ps_log2;
+        int page = a.block_table[(long)b * a.pages_per_seq + (r >> a.ps_log2)];
+        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+        i = (((long)page * a.G + g) * ps + (r & (ps - 1))) * a.D + d;
+    } else {
+        i = ((long)bg * a.Tk + (L - 1)) * a.D + d;
+    }
     const float k = load_f32(static_cast<const QT *>(a.k_new), (long)bg * a.D + d);
     const float v = load_f32(static_cast<const QT *>(a.v_new), (long)bg * a.D + d);
     if constexpr (FP8) {

@@ -156,6 +156,35 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       float scale, hipStream_t stream, const gqa_opts *opts);
 
 /*
+ * Single-token decode over a paged KV cache: the same computation as gqa_decode, with the
+ * cache rows of each sequence held in fixed-size pages that a block table maps ["GQA
+ * revolution ...", section on split-KV block computation, whose work-split heuristic takes a
+ * page size and an is-paged flag; the pages say nothing more of the layout, so the layout
+ * below is this library's reading].
+ *
+ *   k_pages, v_pages [num_pages, G, page_size, D]   kv_dtype; page p holds page_size
+ *                                                   consecutive rows of every KV head
+ *   block_table      [B, pages_per_seq] int32 (device)
+ *
+ * Row t of sequence b and KV head g is k_pages[block_table[b][t / page_size]][g][t % page_size]
+ * (likewise v). The capacity is pages_per_seq * page_size rows per sequence and replaces
+ * opts->kv_capacity; seq_lens are read as in gqa_decode against that capacity. page_size is a
+ * power of two from 16 to 2^20. Only the table entries that cover rows 0 .. seq_lens[b]-1 are
+ * used for the result; entries outside 0 .. num_pages-1 are clamped into that range (no
+ * out-of-bounds access; the result is then unspecified). Pages may be shared or unused.
+ *
+ * Every option of gqa_decode applies (dtypes, fp8 scales per (sequence, KV head), workspace
+ * of gqa_decode_workspace_size() for kv_capacity = pages_per_seq * page_size, layout, cache
+ * append through opts->k_new / v_new, which writes the row's page). Kernel family: matrix
+ * cores only (bf16 q with a bf16 or fp8 cache, D = 128); other paths and dtypes return
+ * GQA_ERR_UNSUPPORTED.
+ */
+gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                            const int32_t *seq_lens, void *out, int B, int H, int G, int D, float scale,
+                            int page_size, int pages_per_seq, int num_pages, hipStream_t stream,
+                            const gqa_opts *opts);
+
+/*
  * Prefill: attention of every position of a sequence over the same sequence's keys
  * (compute-bound [GQA paper digest page, introduction and section "QA"]).
  *

@@ -172,6 +172,32 @@ class Oracle:
         k, v = self.decode_kv_f64(case)
         return self.decode_arrays(case.q, k, v, case.seq_lens.numpy(), case.scale)
 
+    def paged_kv(self, case):
+        """The logical caches [B, G, pages_per_seq * page_size, D] of a paged case: row t of
+        (b, g) is row t mod page_size of page block_table[b, t div page_size]. Returns tensors of
+        the case's cache dtype, so decode_kv_f64 and append read them as a contiguous case."""
+        kp, vp, bt = case.k_pages, case.v_pages, case.block_table.to(torch.int64)
+        B, pps = bt.shape
+        ps = kp.shape[2]
+        t = torch.arange(pps * ps)
+        page = bt[:, t // ps]                       # [B, T]
+        off = (t % ps).expand(B, -1)                # [B, T]
+        # pool[page, :, off] for every (b, t) -> [B, T, G, D] -> [B, G, T, D]
+        gather = lambda pool: pool[page, :, off].permute(0, 2, 1, 3).contiguous()
+        return gather(kp), gather(vp)
+
+    def contiguous_case(self, case):
+        """A workloads.DecodeCase-like view of a paged case, with the logical caches."""
+        import types
+        k, v = self.paged_kv(case)
+        return types.SimpleNamespace(q=case.q, k_cache=k, v_cache=v, seq_lens=case.seq_lens, scale=case.scale,
+                                     q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                                     v_scale=case.v_scale, name=case.name)
+
+    def decode_paged(self, case) -> np.ndarray:
+        """Oracle output [B, H, D] (float64) for a paged case: the decode of its logical caches."""
+        return self.decode(self.contiguous_case(case))
+
     def decode_rows(self, case, rows, kv=None) -> np.ndarray:
         """Oracle output for selected rows (b*H + h) -> [len(rows), D]."""
         k, v = kv if kv is not None else self.decode_kv_f64(case)
@@ -244,6 +270,9 @@ def to_f64(x) -> np.ndarray:
 # Module-level shortcuts onto the default build.
 def decode(case): return load().decode(case)
 def decode_rows(case, rows, kv=None): return load().decode_rows(case, rows, kv)
+def decode_paged(case): return load().decode_paged(case)
+def paged_kv(case): return load().paged_kv(case)
+def contiguous_case(case): return load().contiguous_case(case)
 def decode_arrays(*a): return load().decode_arrays(*a)
 def decode_kv_f64(case): return load().decode_kv_f64(case)
 def prefill(case): return load().prefill(case)

@@ -157,3 +157,31 @@ def test_split_queries(lib):
     # invalid sizes
     assert gqa.decode_num_splits(0, 8, 2, 64, 10) == 0
     assert gqa.decode_workspace_size(1, 6, 4, 64, 10) == 2 ** 64 - 1
+
+
+def _paged(lib, B=2, H=8, G=2, D=128, scale=0.1, page_size=16, pps=4, num_pages=8,
+           ptrs=(FAKE,) * 6, **opt):
+    o = gqa.new_opts(**opt)
+    return lib.gqa_decode_paged(*ptrs, B, H, G, D, scale, page_size, pps, num_pages, None, ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(FAKE, FAKE, FAKE, 0, FAKE, FAKE)), INV),     # no block table
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, 0, FAKE)), INV),
+    (dict(page_size=8), INV), (dict(page_size=48), INV), (dict(page_size=0), INV), (dict(page_size=1 << 21), INV),
+    (dict(pps=0), INV), (dict(num_pages=0), INV),
+    (dict(page_size=1 << 20, pps=1 << 12), INV),              # capacity beyond 2^31 rows
+    (dict(path=1), UNS), (dict(path=2), UNS),                 # matrix-core family only
+    (dict(q_dtype=0, kv_dtype=0), UNS), (dict(D=64), UNS),
+    (dict(k_new=FAKE), INV),
+    (dict(kv_dtype=2), INV),                                  # fp8 without scales
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), WSP),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert _paged(lib, **kw) == code
+
+
+def test_decode_paged_ignores_kv_capacity(lib):
+    # kv_capacity comes from the page geometry: an unset opts.kv_capacity (0) is fine, and the
+    # call proceeds to the workspace check.
+    assert _paged(lib, kv_capacity=0, num_splits=4, workspace=FAKE, workspace_bytes=16) == WSP

@@ -162,6 +162,75 @@ def make_decode(B, H, G, D, seq_lens, T_cap=None, q_dtype=BF16, kv_dtype=BF16, s
                       k_scale=k_scale, v_scale=v_scale)
 
 
+@dataclass
+class PagedDecodeCase:
+    """A decode case whose cache rows live in pages: row t of (b, g) is row t % page_size of
+    page block_table[b, t // page_size] of the pools [num_pages, G, page_size, D]."""
+
+    name: str
+    q: torch.Tensor            # [B, H, D]
+    k_pages: torch.Tensor      # [num_pages, G, page_size, D] kv_dtype
+    v_pages: torch.Tensor
+    block_table: torch.Tensor  # [B, pages_per_seq] int32
+    seq_lens: torch.Tensor     # [B] int32
+    scale: float
+    q_dtype: str
+    kv_dtype: str
+    k_scale: Optional[torch.Tensor] = None   # [B*G] float32, fp8 only
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def D(self): return self.q.shape[2]
+    @property
+    def G(self): return self.k_pages.shape[1]
+    @property
+    def page_size(self): return self.k_pages.shape[2]
+    @property
+    def num_pages(self): return self.k_pages.shape[0]
+    @property
+    def pages_per_seq(self): return self.block_table.shape[1]
+    @property
+    def T_cap(self): return self.pages_per_seq * self.page_size
+
+
+def make_paged(case: DecodeCase, page_size: int, seed: int = 0, spare_pages: Optional[int] = None,
+               name: Optional[str] = None) -> PagedDecodeCase:
+    """Scatter a contiguous decode case into shuffled pages of ``page_size`` rows.
+
+    pages_per_seq = ceil(T_cap / page_size); the logical cache is padded to that many whole
+    pages with poison (NaN, or the fp8 NaN code); ``spare_pages`` (default B) extra pages, all
+    poison, join the pool. A ``torch.randperm`` of the pool (generator seeded with ``seed``)
+    gives the physical page of each (sequence, logical page). Scales are unchanged."""
+    B, G, T_cap, D = case.k_cache.shape
+    pps = -(-T_cap // page_size)
+    spare = B if spare_pages is None else spare_pages
+    num_pages = B * pps + spare
+    perm = torch.randperm(num_pages, generator=_gen(seed))
+    table = perm[:B * pps].reshape(B, pps).to(torch.int32)
+
+    def scatter(cache):
+        raw = cache.view(torch.uint8) if cache.dtype == torch.float8_e4m3fn else cache
+        pool = torch.empty((num_pages, G, page_size, D), dtype=raw.dtype)
+        if raw.dtype == torch.uint8:
+            pool.fill_(0x7F)
+        else:
+            pool.fill_(float("nan"))
+        for b in range(B):
+            for p in range(pps):
+                rows = raw[b, :, p * page_size:(p + 1) * page_size]
+                pool[int(table[b, p]), :, :rows.shape[1]] = rows
+        return pool.view(torch.float8_e4m3fn) if cache.dtype == torch.float8_e4m3fn else pool
+
+    return PagedDecodeCase(name=name or f"{case.name}_paged{page_size}", q=case.q, k_pages=scatter(case.k_cache),
+                           v_pages=scatter(case.v_cache), block_table=table, seq_lens=case.seq_lens,
+                           scale=case.scale, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+                           k_scale=case.k_scale, v_scale=case.v_scale)
+
+
 def make_prefill(B, H, G, D, T, dtype=BF16, causal=True, seed=0, name="prefill",
                  scale=None) -> PrefillCase:
     g = _gen(seed)
