@@ -53,30 +53,41 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of every kernel source; counters taken on other sources do not apply."""
+# Sources of the kernels that each kind of call runs (host layer and shared headers included).
+_COMMON_SOURCES = ("gqa_api.hip", "gqa_internal.h", "dtypes.h", "mfma_util.h")
+_FAMILY_SOURCES = {
+    "decode": _COMMON_SOURCES + ("decode_mfma.hip", "splitkv.h", "splitkv_combine.hip", "kv_append.hip"),
+    "prefill": _COMMON_SOURCES + ("prefill_mfma.hip",),
+}
+
+
+def kernel_sources_sha256(family: str) -> str:
+    """Hash of the sources of one kernel family; counters taken on other sources do not apply."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(_FAMILY_SOURCES[family]):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from recorded FETCH_SIZE/WRITE_SIZE counters, scaled by the same
-    counters on a plain copy of known size; None when absent or taken on other sources."""
+    counters on a plain copy of known size; None when absent or taken on other sources of the
+    workload's kernel family."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != kernel_sources_sha256():
-        return None
     w = rec.get("workloads", {}).get(workload)
-    return None if w is None else w.get("traffic_bytes_per_launch")
+    if w is None:
+        return None
+    family = "prefill" if "prefill" in workload else "decode"
+    if w.get("sources_sha256") != kernel_sources_sha256(family):
+        return None
+    return w.get("traffic_bytes_per_launch")
 
 
 # ------------------------------------------------------------------------------------
