@@ -74,6 +74,9 @@ class Oracle:
         lib.gqa_oracle_prefill_rows.argtypes = ([_dp, _dp, _dp] + [ctypes.c_int] * 5 +
                                                 [ctypes.c_double, ctypes.c_int, _lp, ctypes.c_long, _dp])
         lib.gqa_oracle_prefill_rows.restype = ctypes.c_int
+        lib.gqa_oracle_prefill_cached.argtypes = ([_dp, _dp, _dp, _ip, _dp] + [ctypes.c_int] * 5 +
+                                                  [ctypes.c_long, ctypes.c_double, ctypes.c_int])
+        lib.gqa_oracle_prefill_cached.restype = ctypes.c_int
         lib.gqa_oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
         lib.gqa_oracle_e4m3fn_value.restype = ctypes.c_double
         lib.gqa_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
@@ -230,6 +233,25 @@ class Oracle:
         """Oracle output [B, H, T, D] (float64) for a workloads.PrefillCase."""
         return self.prefill_arrays(case.q, case.k, case.v, case.scale, case.causal)
 
+    def prefill_cached_arrays(self, q, k_cache, v_cache, seq_lens, scale, causal) -> np.ndarray:
+        """Chunk of Tq queries [B,H,Tq,D] against caches [B,G,T_cap,D] holding seq_lens[b] rows."""
+        q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
+        B, H, Tq, D = q.shape
+        _, G, T_cap, _ = k.shape
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        out = np.empty((B, H, Tq, D), dtype=np.float64)
+        rc = self.lib.gqa_oracle_prefill_cached(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(sl, _ip),
+                                                _ptr(out, _dp), B, Tq, H, G, D, T_cap, float(scale),
+                                                int(bool(causal)))
+        if rc != 0:
+            raise ValueError(f"oracle prefill_cached rejected its arguments (code {rc})")
+        return out
+
+    def prefill_cached(self, case) -> np.ndarray:
+        """Oracle output [B, H, Tq, D] (float64) for a workloads.ChunkCase."""
+        return self.prefill_cached_arrays(case.q, case.k_cache, case.v_cache, case.seq_lens.numpy(), case.scale,
+                                          case.causal)
+
     def prefill_rows(self, case, rows, f64=None) -> np.ndarray:
         """Oracle output for selected rows ((b*H + h)*T + i) -> [len(rows), D]."""
         q, k, v = f64 if f64 is not None else (_f64(case.q), _f64(case.k), _f64(case.v))
@@ -278,6 +300,8 @@ def decode_kv_f64(case): return load().decode_kv_f64(case)
 def prefill(case): return load().prefill(case)
 def prefill_rows(case, rows, f64=None): return load().prefill_rows(case, rows, f64)
 def prefill_arrays(*a): return load().prefill_arrays(*a)
+def prefill_cached(case): return load().prefill_cached(case)
+def prefill_cached_arrays(*a): return load().prefill_cached_arrays(*a)
 def dequant_e4m3fn(codes, scales): return load().dequant_e4m3fn(codes, scales)
 def e4m3fn_value(code): return load().e4m3fn_value(code)
 def e4m3fn_encode(q): return load().e4m3fn_encode(q)

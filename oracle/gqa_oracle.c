@@ -202,6 +202,49 @@ int gqa_oracle_prefill(const double *q, const double *k, const double *v, double
     return fail ? 2 : 0;
 }
 
+/*
+ * Prefill of a chunk of Tq query positions against a cache that already holds earlier
+ * tokens ("LLM principles -- code implementation of multi-head attention (MQA and GQA)",
+ * sections 3 and 5: new keys and values are concatenated to the cache before the scores, and
+ * the causal mask hides later keys). q, out [B,H,Tq,D]; k, v [B,G,T_cap,D]; seq_lens[b] = L_b
+ * counts every valid cache row, the chunk included, so query i of sequence b sits at
+ * position p = L_b - Tq + i. It sees keys 0 .. p (causal) or 0 .. L_b - 1 (not causal), never
+ * beyond L_b - 1; L_b is clamped to 0 .. T_cap as in decode. A row that sees no key (p < 0)
+ * is zero. With Tq = 1 this is decode; with L_b = Tq = T_cap it is the plain prefill.
+ */
+int gqa_oracle_prefill_cached(const double *q, const double *k, const double *v, const int32_t *seq_lens,
+                              double *out, int B, int Tq, int H, int G, int D, long T_cap, double scale,
+                              int causal)
+{
+    if (B < 1 || Tq < 1 || H < 1 || G < 1 || D < 1 || T_cap < 1 || H % G != 0) return 1;
+    long row, nrow = (long)B * H * Tq;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)T_cap);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (row = 0; row < nrow; ++row) {
+                int i = (int)(row % Tq);
+                long bh = row / Tq;
+                int b = (int)(bh / H), h = (int)(bh % H);
+                int g = kv_head_of(h, H, G);
+                long L = seq_lens[b] < 0 ? 0 : (seq_lens[b] > T_cap ? T_cap : seq_lens[b]);
+                long p = L - Tq + i;
+                long n = causal ? (p + 1 < L ? p + 1 : L) : L;
+                const double *K = k + ((long)b * G + g) * T_cap * D;
+                const double *V = v + ((long)b * G + g) * T_cap * D;
+                attend_row(q + row * D, K, V, n, D, scale, out + row * D, s);
+            }
+            free(s);
+        }
+    }
+    return fail ? 2 : 0;
+}
+
 /* Prefill, selected rows only: rows[r] = (b*H + h)*T + i; out_rows[r][D]. */
 int gqa_oracle_prefill_rows(const double *q, const double *k, const double *v, int B, int T,
                             int H, int G, int D, double scale, int causal, const int64_t *rows,

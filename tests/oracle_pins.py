@@ -330,8 +330,52 @@ def pin_e4m3fn_encoder(orc):
     assert orc.quant_e4m3fn([np.float32(1.3)], np.float32(0.37))[0] == orc.e4m3fn_encode(q), "fp32 quotient"
 
 
+def pin_chunk_special_cases(orc):
+    """Chunked prefill reduces to decode (Tq = 1) and to plain prefill (L = Tq = T_cap), both
+    exactly (same rows, same key counts, same summation order)."""
+    B, H, G, D, T = 2, 8, 2, 16, 20
+    q, k, v = _rand((B, H, T, D), 201), _rand((B, G, T, D), 202), _rand((B, G, T, D), 203)
+    lens = np.array([T, 7], dtype=np.int32)
+    one = orc.prefill_cached_arrays(q[:, :, :1], k, v, lens, 0.3, True)[:, :, 0]
+    assert np.array_equal(one, orc.decode_arrays(q[:, :, 0], k, v, lens, 0.3)), "Tq = 1 is decode"
+    full = np.full(B, T, dtype=np.int32)
+    for causal in (True, False):
+        got = orc.prefill_cached_arrays(q, k, v, full, 0.3, causal)
+        assert np.array_equal(got, orc.prefill_arrays(q, k, v, 0.3, causal)), f"whole chunk, causal={causal}"
+
+
+def pin_chunks_compose_prefill(orc):
+    """Chunks [0,5), [5,17), [17,24) against a growing cache give the causal prefill rows."""
+    B, H, G, D, T, T_cap = 2, 8, 2, 16, 24, 30
+    q, k, v = _rand((B, H, T, D), 211), _rand((B, G, T, D), 212), _rand((B, G, T, D), 213)
+    full = orc.prefill_arrays(q, k, v, 0.25, True)
+    for s, e in ((0, 5), (5, 17), (17, 24)):
+        kc = torch.full((B, G, T_cap, D), float("nan"), dtype=torch.float64)
+        vc = torch.full((B, G, T_cap, D), float("nan"), dtype=torch.float64)
+        kc[:, :, :e] = k[:, :, :e]
+        vc[:, :, :e] = v[:, :, :e]
+        got = orc.prefill_cached_arrays(q[:, :, s:e], kc, vc, np.full(B, e, dtype=np.int32), 0.25, True)
+        assert np.array_equal(got, full[:, :, s:e]), f"chunk [{s},{e})"
+
+
+def pin_chunk_short_cache(orc):
+    """L < Tq: rows before position 0 see no key (zero); the row at position 0 sees key 0 only
+    (its output is v[0]). Not causal: every row sees all L keys, as a decode at length L."""
+    B, H, G, D, Tq, T_cap = 1, 4, 2, 8, 6, 6
+    q, k, v = _rand((B, H, Tq, D), 221), _rand((B, G, T_cap, D), 222), _rand((B, G, T_cap, D), 223)
+    L = 3
+    lens = np.array([L], dtype=np.int32)
+    got = orc.prefill_cached_arrays(q, k, v, lens, 0.5, True)
+    assert np.all(got[:, :, :Tq - L] == 0), "rows before position 0"
+    for h in range(H):
+        assert np.array_equal(got[0, h, Tq - L], v[0, h // 2, 0].numpy()), "position 0 sees key 0 only"
+    nc = orc.prefill_cached_arrays(q, k, v, lens, 0.5, False)
+    for i in range(Tq):
+        assert np.array_equal(nc[:, :, i], orc.decode_arrays(q[:, :, i], k, v, lens, 0.5)), f"row {i}"
+
+
 ALL_PINS = [pin_hand_worked, pin_toy_three_ways, pin_sdpa_prefill, pin_sdpa_decode, pin_mha, pin_mqa,
             pin_group_materialise, pin_identical_keys_mean_v, pin_value_constant_per_head, pin_single_row,
             pin_shift_invariance, pin_permutation_invariance, pin_linear_and_convex,
             pin_incremental_decode_equals_prefill, pin_nan_padding, pin_length_readings, pin_e4m3fn_decoder,
-            pin_e4m3fn_encoder]
+            pin_e4m3fn_encoder, pin_chunk_special_cases, pin_chunks_compose_prefill, pin_chunk_short_cache]

@@ -25,6 +25,8 @@ MUTANTS = [
     ("fp8_quotient_inverted", "codes[i] = gqa_oracle_e4m3fn_encode(x[i] / scale);",
      "codes[i] = gqa_oracle_e4m3fn_encode(x[i] * scale);"),
     ("fp8_sign_dropped", "return (uint8_t)(best | (neg << 7));", "return (uint8_t)best;"),
+    ("chunk_offset_off_by_one", "long p = L - Tq + i;", "long p = L - Tq + i + 1;"),
+    ("chunk_not_causal_masks", "long n = causal ? (p + 1 < L ? p + 1 : L) : L;", "long n = p + 1 < L ? p + 1 : L;"),
 ]
 
 

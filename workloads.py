@@ -231,6 +231,56 @@ def make_paged(case: DecodeCase, page_size: int, seed: int = 0, spare_pages: Opt
                            k_scale=case.k_scale, v_scale=case.v_scale)
 
 
+@dataclass
+class ChunkCase:
+    """Prefill of a chunk of Tq query positions against a cache: query i of sequence b sits at
+    position seq_lens[b] - Tq + i; the cache already holds the chunk's own keys and values."""
+
+    name: str
+    q: torch.Tensor          # [B, H, Tq, D]
+    k_cache: torch.Tensor    # [B, G, T_cap, D]
+    v_cache: torch.Tensor
+    seq_lens: torch.Tensor   # [B] int32, valid cache rows (chunk included)
+    scale: float
+    causal: bool
+    dtype: str
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def Tq(self): return self.q.shape[2]
+    @property
+    def D(self): return self.q.shape[3]
+    @property
+    def G(self): return self.k_cache.shape[1]
+    @property
+    def T_cap(self): return self.k_cache.shape[2]
+
+
+def make_chunk(B, H, G, D, Tq, seq_lens, T_cap=None, dtype=BF16, causal=True, seed=0, name="chunk",
+               scale=None) -> ChunkCase:
+    """Chunked-prefill inputs. Draw order: Q [B,H,Tq,D], then K and V over the whole cache
+    [B,G,T_cap,D]; cache rows at or beyond seq_lens[b] are NaN."""
+    g = _gen(seed)
+    lens = torch.tensor(list(seq_lens) if not isinstance(seq_lens, int) else [seq_lens] * B, dtype=torch.int32)
+    if T_cap is None:
+        T_cap = max(int(lens.max()), 1)
+    q = _randn((B, H, Tq, D), g)
+    k = _randn((B, G, T_cap, D), g)
+    v = _randn((B, G, T_cap, D), g)
+    for b in range(B):
+        L = int(min(max(int(lens[b]), 0), T_cap))
+        k[b, :, L:] = float("nan")
+        v[b, :, L:] = float("nan")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    td = _TORCH_DTYPE[dtype]
+    return ChunkCase(name=name, q=q.to(td), k_cache=k.to(td), v_cache=v.to(td), seq_lens=lens, scale=float(scale),
+                     causal=causal, dtype=dtype)
+
+
 def make_prefill(B, H, G, D, T, dtype=BF16, causal=True, seed=0, name="prefill",
                  scale=None) -> PrefillCase:
     g = _gen(seed)
