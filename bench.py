@@ -8,7 +8,8 @@ workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H
 D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
 B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown", and so are the headline
 and fp8 decodes with the current token's KV-cache append done by the same call ("+append"),
-and three decodes over a cache in shuffled 16-row pages ("_paged16").
+three decodes over a cache in shuffled 16-row pages ("_paged16"), and a prefill of the last
+512 positions of 4096-token sequences against the cache of the first 3584.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations. Each step reads the next of several replicas of its inputs, together
@@ -163,6 +164,49 @@ def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
             gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, **new)
 
     return step, nrep, out
+
+
+def chunk_flops(c: W.ChunkCase) -> int:
+    """Causal: query i of a sequence of L keys sees L - Tq + i + 1 keys; 4*D flops per pair."""
+    lens = c.seq_lens.clamp(0, c.T_cap).to(torch.int64)
+    pairs = 0
+    for L in lens.tolist():
+        if c.causal:
+            pairs += sum(max(0, min(L, L - c.Tq + i + 1)) for i in range(c.Tq))
+        else:
+            pairs += L * c.Tq
+    return 4 * c.H * c.D * pairs
+
+
+def bench_chunk(gqa, c: W.ChunkCase, steps, warmup, dev):
+    kv_alloc = 2 * c.k_cache.numel() * c.k_cache.element_size()
+    nrep = max(1, math.ceil(COLD_BYTES / kv_alloc))
+    base = [c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)]
+    reps = [base] + [[t.clone() for t in base] for _ in range(nrep - 1)]
+    lens = c.seq_lens.to(dev)
+    out = torch.empty_like(base[0])
+    state = {"i": 0}
+
+    def step():
+        q, k, v = reps[state["i"] % nrep]
+        state["i"] += 1
+        gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal)
+
+    t = time_steps(step, steps, warmup)
+    fl = chunk_flops(c)
+    s = t["ms_per_step"] * 1e-3
+    achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
+    esz = 2
+    lsum = int(c.seq_lens.clamp(0, c.T_cap).sum())
+    return {
+        "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "Tq": c.Tq, "T_cap": c.T_cap,
+        "seq_lens": c.seq_lens.tolist(), "causal": c.causal, "flops": fl,
+        "algorithmic_bytes": esz * (2 * c.q.numel() + 2 * lsum * c.G * c.D), "tflops": fl / s / 1e12,
+        "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
+        "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+    }
 
 
 def make_prefill_runner(gqa, c: W.PrefillCase, dev):
@@ -366,6 +410,12 @@ def main():
             if W.WORKLOADS[name] is not W.causal_prefill_2048:
                 _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
                 breakdown[name + "+append"] = r
+        # Prefill of a 512-token chunk against a 3584-token cache.
+        cc = W.chunked_prefill_512_of_4096(0)
+        log(f"[bench] {cc.name}")
+        r = bench_chunk(gqa, cc, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
+        log(f"[bench] {cc.name}: {json.dumps(r)}")
+        breakdown[cc.name] = r
         # The same decodes over a cache in shuffled pages of 16 rows.
         for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
             pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)

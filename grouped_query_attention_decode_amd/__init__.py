@@ -9,6 +9,8 @@ not gfx950, calls raise.
     decode_paged(q, k_pages, v_pages, block_table, seq_lens, ...)
                                                  pools [num_pages,G,page_size,D], table [B,pages_per_seq]
     prefill(q, k, v, causal=True, ...)           q [B,H,T,D], k/v [B,G,T,D]
+    prefill_cached(q, k_cache, v_cache, seq_lens, causal=True, ...)
+                                                 q [B,H,Tq,D] against caches [B,G,T_cap,D]
 """
 
 from __future__ import annotations
@@ -19,7 +21,7 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
-__all__ = ["decode", "decode_paged", "prefill", "decode_num_splits", "decode_workspace_size", "status_string",
+__all__ = ["decode", "decode_paged", "prefill", "prefill_cached", "decode_num_splits", "decode_workspace_size", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
@@ -89,6 +91,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_decode_paged.restype = i
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_prefill_cached.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_prefill_cached.restype = i
     lib.gqa_prefill.restype = i
     lib.gqa_decode_num_splits.argtypes = [i] * 7
     lib.gqa_decode_num_splits.restype = i
@@ -272,4 +276,43 @@ def prefill(q, k, v, out=None, scale=None, causal=True, path="auto", stream=None
                                ctypes.byref(o))
     if st != GQA_OK:
         raise GqaError(st, "gqa_prefill")
+    return out
+
+
+def prefill_cached(q, k_cache, v_cache, seq_lens, out=None, scale=None, causal=True, k_scale=None, v_scale=None,
+                   path="auto", stream=None):
+    """Prefill of a chunk of Tq positions against a cache. Returns ``out`` [B, H, Tq, D].
+
+    q [B, H, Tq, D]; caches [B, G, T_cap, D] already holding the chunk's keys and values at rows
+    seq_lens[b]-Tq .. seq_lens[b]-1; query i of sequence b sits at position seq_lens[b]-Tq+i."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n)
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [B,H,Tq,D] and k_cache, v_cache [B,G,T_cap,D]")
+    B, H, Tq, D = q.shape
+    Bk, G, T_cap, Dk = k_cache.shape
+    if Bk != B or Dk != D or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens (int32 [B])")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kv_code = _dtype_code(k_cache, "k_cache")
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap, path=PATHS[path])
+    if kv_code == DTYPES["fp8_e4m3fn"]:
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 caches need k_scale and v_scale")
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need_cuda(t, n)
+            if t.dtype != torch.float32 or t.numel() != B * G:
+                raise ValueError(f"{n} must be float32 [B*G]")
+        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    st = library().gqa_prefill_cached(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                      out.data_ptr(), B, Tq, H, G, D, float(scale), int(bool(causal)),
+                                      _stream_handle(stream, q.device), ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_prefill_cached")
     return out

@@ -9,7 +9,9 @@
 // (GQA)"; "LLM principles -- code implementation of multi-head attention (MQA and
 // GQA)", section 5]. Scores use the online (running max / running sum) form of the
 // softmax, in base 2 with log2(e) folded into the scale; that equals the page's
-// softmax(QK^T / sqrt(d)) V (same page, section 3) in exact arithmetic.
+// softmax(QK^T / sqrt(d)) V (same page, section 3) in exact arithmetic. Modes: decode (one
+// query row at the sequence's last position), prefill, and prefill of a chunk of Tq queries
+// against a cache of seq_lens[b] rows (the chunk's rows at the end, causal from there).
 #include "dtypes.h"
 #include "gqa_internal.h"
 
@@ -47,8 +49,9 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, int 
     const int split = blockIdx.y;
     const int rows = hpw * tm;
 
-    // Key range of this workgroup.
-    int kb, ke, dec_pos = 0;
+    // Key range of this workgroup. A chunk against a cache (a.cached) holds the last Tq of
+    // L positions: query row i sits at position off + i, off = L - Tq (0 for a plain prefill).
+    int kb, ke, dec_pos = 0, off = 0;
     if (a.decode) {
         int L = a.seq_lens[b];
         L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
@@ -56,9 +59,16 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, int 
         kb = split * a.split_len;
         ke = kb + a.split_len < L ? kb + a.split_len : L;
     } else {
+        int L = a.Tk;
+        if (a.cached) {
+            L = a.seq_lens[b];
+            L = L < 0 ? 0 : (L > a.Tk ? a.Tk : L);
+            off = L - a.Tq;
+        }
         kb = 0;
-        const int last = qt * tm + tm - 1;
-        ke = a.causal ? (last + 1 < a.Tk ? last + 1 : a.Tk) : a.Tk;
+        const int last = off + qt * tm + tm - 1;
+        ke = a.causal ? (last + 1 < L ? last + 1 : L) : L;
+        ke = ke < 0 ? 0 : ke;
     }
 
     for (int r = tid; r < rows; r += kThreads) {
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, int 
         for (int pidx = tid; pidx < rows * kTileN; pidx += kThreads) {
             const int r = pidx / kTileN, j = pidx % kTileN;
             float s = -INFINITY;
-            const bool live = j < n && head_s[r] >= 0 && (a.decode || !a.causal || t0 + j <= pos_s[r]);
+            const bool live = j < n && head_s[r] >= 0 && (a.decode || !a.causal || t0 + j <= off + pos_s[r]);
             if (live) {
                 float dot = 0.f;
                 for (int d = 0; d < D; ++d) dot += q_s[r * D + d] * k_s[j * D + d];

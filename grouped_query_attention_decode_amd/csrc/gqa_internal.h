@@ -32,6 +32,8 @@ struct AttnArgs {
     int Tk;                   // key rows allocated per (b, g): T_cap or T
     int causal;               // prefill: 1 = keys j <= i only
     int decode;               // 1 = keys limited by seq_lens[b], query at row L-1
+    int cached;               // prefill against a cache: keys limited by seq_lens[b], query i at
+                              // position seq_lens[b] - Tq + i (Tk = T_cap); 0 = plain prefill
     int num_splits;           // decode: key ranges per (b, g) (1 = write out directly); with the
                               // flat layout, the partial slots per query head
     int split_len;            // decode, uniform layout: keys per range

@@ -26,6 +26,10 @@
 // the next tile streams in while the current one is multiplied. Causal tiles entirely above
 // the diagonal are skipped; position tiles are issued heaviest first, and all blocks of one
 // (b, g) land on one XCD (block i runs on XCD i mod 8), so its K/V stays in that L2.
+// Chunk against a cache (CACHED): the T queries are the last T of the sequence's L_b
+// positions, so query i sits at position L_b - T + i; keys come from the cache [B,G,T_cap,D]
+// and stop at L_b; the causal diagonal moves by L_b - T ("LLM principles -- code ...",
+// sections 3 and 5: keys concatenated to the cache, later keys masked).
 #include "dtypes.h"
 #include "gqa_internal.h"
 #include "mfma_util.h"
@@ -82,7 +86,7 @@ __device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k
     }
 }
 
-template <int R, bool CAUSAL>
+template <int R, bool CAUSAL, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     constexpr int P = kRows / R;  // positions per workgroup
     __shared__ __attribute__((aligned(16))) char k_lds0[kTileBytes];
@@ -100,6 +104,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     const int pt = CAUSAL ? npt - 1 - (int)(blockIdx.x / nbg) : (int)(blockIdx.x / nbg);
     const int b = bg / G, g = bg % G;
     const int p0 = pt * P;
+    // Keys of this sequence, and the position of query row 0: a chunk against a cache holds
+    // the last T of Lb positions; a plain prefill is Lb = T, offset 0.
+    const int Tk = CACHED ? a.Tk : T;
+    int Lb = T;
+    if constexpr (CACHED) {
+        const int l = a.seq_lens[b];
+        Lb = __builtin_amdgcn_readfirstlane(l < 0 ? 0 : (l > Tk ? Tk : l));
+    }
+    const int off = Lb - T;
 
     // This lane's query row.
     const int wr = 32 * wave + (lane & 31);  // row inside the workgroup
@@ -124,13 +137,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) qT[ks][e] ^= qsign;
     }
 
-    const char *kbase = static_cast<const char *>(a.k) + (long)bg * T * kRowBytes;
-    const char *vbase = static_cast<const char *>(a.v) + (long)bg * T * kRowBytes;
+    const char *kbase = static_cast<const char *>(a.k) + (long)bg * Tk * kRowBytes;
+    const char *vbase = static_cast<const char *>(a.v) + (long)bg * Tk * kRowBytes;
 
-    // Keys this workgroup needs, and the smallest position held by this wave.
-    const int wg_last = p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1;
-    const int nkt = CAUSAL ? wg_last / kBN + 1 : (T + kBN - 1) / kBN;
-    const int wave_min_pos = P >= 32 ? p0 + (32 * wave) % P : p0;
+    // Keys this workgroup needs (absolute positions), and the smallest position of this wave.
+    const int wg_last = off + (p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1);
+    const int nkt = CAUSAL ? (wg_last < 0 ? 0 : wg_last / kBN + 1) : (Lb + kBN - 1) / kBN;
+    const int wave_min_pos = off + (P >= 32 ? p0 + (32 * wave) % P : p0);
+    const int kmax = Lb > 0 ? Lb : 1;  // tile loads clamp to the last valid row (row 0 when none)
 
     f32x16_t o[4];
 #pragma unroll
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
                 for (int e = 0; e < 16; ++e) {
                     const int i = e >> 2, j = e & 3;
                     const int key = k0 + 32 * kh + 16 * (i >> 1) + 8 * hl + 4 * (i & 1) + j;
-                    const bool vis = key < T && (!CAUSAL || key <= pos);
+                    const bool vis = key < Lb && (!CAUSAL || key <= off + pos);
                     s[kh][e] = vis ? s[kh][e] : -INFINITY;
                 }
         }
@@ -239,25 +253,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     };
 
     auto tile_needs_mask = [&](int k0) {
-        return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > T);
+        return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > Lb);
     };
 
-    load_tile(k_lds0, kbase, 0, T, wave, lane);
-    load_tile(v_lds0, vbase, 0, T, wave, lane);
+    load_tile(k_lds0, kbase, 0, kmax, wave, lane);
+    load_tile(v_lds0, vbase, 0, kmax, wave, lane);
     wait_vmem_all();
     __syncthreads();
     for (int kt = 0; kt < nkt; kt += 2) {
         if (kt + 1 < nkt) {
-            load_tile(k_lds1, kbase, (kt + 1) * kBN, T, wave, lane);
-            load_tile(v_lds1, vbase, (kt + 1) * kBN, T, wave, lane);
+            load_tile(k_lds1, kbase, (kt + 1) * kBN, kmax, wave, lane);
+            load_tile(v_lds1, vbase, (kt + 1) * kBN, kmax, wave, lane);
         }
         compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
         wait_vmem_all();
         __syncthreads();
         if (kt + 1 >= nkt) break;
         if (kt + 2 < nkt) {
-            load_tile(k_lds0, kbase, (kt + 2) * kBN, T, wave, lane);
-            load_tile(v_lds0, vbase, (kt + 2) * kBN, T, wave, lane);
+            load_tile(k_lds0, kbase, (kt + 2) * kBN, kmax, wave, lane);
+            load_tile(v_lds0, vbase, (kt + 2) * kBN, kmax, wave, lane);
         }
         compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
         wait_vmem_all();
@@ -287,10 +301,17 @@ hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
     constexpr int P = kRows / R;
     const int npt = (a.Tq + P - 1) / P;
     dim3 grid((unsigned)(a.B * a.G * npt));
-    if (a.causal)
-        hipLaunchKernelGGL((prefill_mfma_kernel<R, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prefill_mfma_kernel<R, false>), grid, dim3(kThreads), 0, stream, a);
+    if (a.cached) {
+        if (a.causal)
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, true>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (a.causal)
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, false>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, false>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

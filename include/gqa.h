@@ -201,6 +201,29 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
                        int H, int G, int D, float scale, int causal, hipStream_t stream,
                        const gqa_opts *opts);
 
+/*
+ * Prefill of a chunk of Tq new positions against a KV cache (chunked prefill; Tq = 1 is
+ * decode): the generalisation of ["LLM principles -- code ...", sections 3 and 5], where the
+ * new keys and values are concatenated to the cache and the causal mask hides later keys.
+ *
+ *   q        [B, H, Tq, D]        q_dtype, the chunk's queries
+ *   k_cache  [B, G, T_cap, D]     kv_dtype, T_cap = opts->kv_capacity (required)
+ *   v_cache  [B, G, T_cap, D]
+ *   seq_lens [B] int32 (device)   valid rows of sequence b, the chunk's own rows included
+ *   out      [B, H, Tq, D]        q_dtype
+ *
+ * The caller has written the chunk's keys and values at rows seq_lens[b]-Tq .. seq_lens[b]-1.
+ * Query i of sequence b sits at position p = seq_lens[b] - Tq + i. causal = 1: it attends to
+ * rows 0 .. p; causal = 0: to rows 0 .. seq_lens[b]-1. seq_lens is read as in gqa_decode (a
+ * value above T_cap is T_cap, below 0 is 0); a query with p < 0 sees no row and its output is
+ * zero. Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16) -- matrix cores for D = 128
+ * and R a power of two up to 64 -- and (BF16, FP8_E4M3FN) with opts->k_scale / v_scale as in
+ * gqa_decode (generic family). D in 1..256.
+ */
+gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                              void *out, int B, int Tq, int H, int G, int D, float scale, int causal,
+                              hipStream_t stream, const gqa_opts *opts);
+
 /* Key ranges per (sequence, KV head) -- with the flat layout, the most partial results one
  * query head can have -- that gqa_decode uses for these sizes with path and layout AUTO
  * (num_splits 0 = the library's own choice, which depends only on these arguments). Returns 0

@@ -248,9 +248,13 @@ class Oracle:
         return out
 
     def prefill_cached(self, case) -> np.ndarray:
-        """Oracle output [B, H, Tq, D] (float64) for a workloads.ChunkCase."""
-        return self.prefill_cached_arrays(case.q, case.k_cache, case.v_cache, case.seq_lens.numpy(), case.scale,
-                                          case.causal)
+        """Oracle output [B, H, Tq, D] (float64) for a workloads.ChunkCase (fp8 caches dequantised
+        with their scales first)."""
+        if case.kv_dtype == "fp8_e4m3fn":
+            k, v = self.dequant_e4m3fn(case.k_cache, case.k_scale), self.dequant_e4m3fn(case.v_cache, case.v_scale)
+        else:
+            k, v = case.k_cache, case.v_cache
+        return self.prefill_cached_arrays(case.q, k, v, case.seq_lens.numpy(), case.scale, case.causal)
 
     def prefill_rows(self, case, rows, f64=None) -> np.ndarray:
         """Oracle output for selected rows ((b*H + h)*T + i) -> [len(rows), D]."""

@@ -185,3 +185,28 @@ def test_decode_paged_ignores_kv_capacity(lib):
     # kv_capacity comes from the page geometry: an unset opts.kv_capacity (0) is fine, and the
     # call proceeds to the workspace check.
     assert _paged(lib, kv_capacity=0, num_splits=4, workspace=FAKE, workspace_bytes=16) == WSP
+
+
+def _chunk(lib, B=2, Tq=16, H=8, G=2, D=128, scale=0.1, causal=1, ptrs=(FAKE,) * 5, opts=True, **opt):
+    fields = dict(kv_capacity=64)
+    fields.update(opt)
+    o = gqa.new_opts(**fields)
+    return lib.gqa_prefill_cached(*ptrs, B, Tq, H, G, D, scale, causal, None, ctypes.byref(o) if opts else None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(FAKE, FAKE, FAKE, 0, FAKE)), INV),      # seq_lens required
+    (dict(ptrs=(0, FAKE, FAKE, FAKE, FAKE)), INV),
+    (dict(opts=False), INV),                            # opts carries kv_capacity
+    (dict(kv_capacity=0), INV), (dict(Tq=0), INV), (dict(B=0), INV),
+    (dict(H=6, G=4), INV), (dict(D=300), INV),
+    (dict(causal=2), INV), (dict(scale=float("nan")), INV),
+    (dict(q_dtype=0, kv_dtype=1), UNS), (dict(q_dtype=2, kv_dtype=2), UNS),
+    (dict(kv_dtype=2), INV),                            # fp8 without scales
+    (dict(path=2), UNS),                                # no vector-ALU prefill
+    (dict(q_dtype=0, kv_dtype=0, path=3), UNS),         # matrix cores: bf16 only
+    (dict(H=12, G=4, path=3), UNS),                     # matrix cores: R a power of two
+    (dict(path=7), INV),
+])
+def test_prefill_cached_rejects(lib, kw, code):
+    assert _chunk(lib, **kw) == code

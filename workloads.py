@@ -243,7 +243,10 @@ class ChunkCase:
     seq_lens: torch.Tensor   # [B] int32, valid cache rows (chunk included)
     scale: float
     causal: bool
-    dtype: str
+    dtype: str                                # q's dtype
+    kv_dtype: str = BF16
+    k_scale: Optional[torch.Tensor] = None    # [B*G] float32, fp8 only
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def B(self): return self.q.shape[0]
@@ -260,9 +263,10 @@ class ChunkCase:
 
 
 def make_chunk(B, H, G, D, Tq, seq_lens, T_cap=None, dtype=BF16, causal=True, seed=0, name="chunk",
-               scale=None) -> ChunkCase:
+               scale=None, kv_dtype=None) -> ChunkCase:
     """Chunked-prefill inputs. Draw order: Q [B,H,Tq,D], then K and V over the whole cache
-    [B,G,T_cap,D]; cache rows at or beyond seq_lens[b] are NaN."""
+    [B,G,T_cap,D]; cache rows at or beyond seq_lens[b] are NaN. kv_dtype FP8 (with bf16 q)
+    stores the caches as E4M3FN codes with per-(b, g) scales, as in make_decode."""
     g = _gen(seed)
     lens = torch.tensor(list(seq_lens) if not isinstance(seq_lens, int) else [seq_lens] * B, dtype=torch.int32)
     if T_cap is None:
@@ -277,8 +281,13 @@ def make_chunk(B, H, G, D, Tq, seq_lens, T_cap=None, dtype=BF16, causal=True, se
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     td = _TORCH_DTYPE[dtype]
+    if kv_dtype == FP8:
+        kc, ks = quantize_fp8_slabs(k, lens)
+        vc, vs = quantize_fp8_slabs(v, lens)
+        return ChunkCase(name=name, q=q.to(td), k_cache=kc, v_cache=vc, seq_lens=lens, scale=float(scale),
+                         causal=causal, dtype=dtype, kv_dtype=FP8, k_scale=ks, v_scale=vs)
     return ChunkCase(name=name, q=q.to(td), k_cache=k.to(td), v_cache=v.to(td), seq_lens=lens, scale=float(scale),
-                     causal=causal, dtype=dtype)
+                     causal=causal, dtype=dtype, kv_dtype=dtype)
 
 
 def make_prefill(B, H, G, D, T, dtype=BF16, causal=True, seed=0, name="prefill",
@@ -357,6 +366,12 @@ def mqa_fp8_long_decode(seed=0) -> DecodeCase:
     """Long-context MQA decode: B8 H32 G1 D128, 32768 cached tokens, fp8-E4M3FN KV."""
     return make_decode(8, 32, 1, 128, 32768, T_cap=32768, kv_dtype=FP8, seed=seed,
                        name="mqa_fp8_decode_B8_L32768")
+
+
+def chunked_prefill_512_of_4096(seed=0) -> ChunkCase:
+    """Chunked prefill: B4 H32 G8 D128, the last 512 positions of 4096-token sequences against
+    the cache holding the first 3584 (and the chunk's own rows), causal, bf16."""
+    return make_chunk(4, 32, 8, 128, 512, 4096, T_cap=4096, seed=seed, name="gqa8_chunked_prefill_B4_Tq512_L4096")
 
 
 WORKLOADS = {
