@@ -77,6 +77,14 @@ class Oracle:
         lib.gqa_oracle_prefill_cached.argtypes = ([_dp, _dp, _dp, _ip, _dp] + [ctypes.c_int] * 5 +
                                                   [ctypes.c_long, ctypes.c_double, ctypes.c_int])
         lib.gqa_oracle_prefill_cached.restype = ctypes.c_int
+        lib.gqa_oracle_int4_value.argtypes = [ctypes.c_int]
+        lib.gqa_oracle_int4_value.restype = ctypes.c_int
+        lib.gqa_oracle_int4_encode.argtypes = [ctypes.c_float]
+        lib.gqa_oracle_int4_encode.restype = ctypes.c_int
+        lib.gqa_oracle_quant_int4.argtypes = [_fp, ctypes.c_float, ctypes.c_long, _u8p]
+        lib.gqa_oracle_quant_int4.restype = None
+        lib.gqa_oracle_dequant_int4.argtypes = [_u8p, _fp, ctypes.c_long, ctypes.c_long, _dp]
+        lib.gqa_oracle_dequant_int4.restype = None
         lib.gqa_oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
         lib.gqa_oracle_e4m3fn_value.restype = ctypes.c_double
         lib.gqa_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
@@ -112,6 +120,30 @@ class Oracle:
                                          _ptr(codes, _u8p))
         return codes
 
+    def int4_value(self, u: int) -> int:
+        return int(self.lib.gqa_oracle_int4_value(int(u)))
+
+    def int4_encode(self, q: float) -> int:
+        return int(self.lib.gqa_oracle_int4_encode(float(q)))
+
+    def quant_int4(self, x, scale: float) -> np.ndarray:
+        """Packed INT4 fields (uint8, half the length) of x / scale, the quotient in fp32."""
+        xn = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        packed = np.empty(xn.shape[:-1] + (xn.shape[-1] // 2,), dtype=np.uint8)
+        self.lib.gqa_oracle_quant_int4(_ptr(xn, _fp), ctypes.c_float(float(np.float32(scale))), xn.size,
+                                       _ptr(packed, _u8p))
+        return packed
+
+    def dequant_int4(self, packed: torch.Tensor, scales: torch.Tensor) -> np.ndarray:
+        """packed [S, ..., D/2] uint8, scales [S] float32 -> float64 [S, ..., D]."""
+        c = np.ascontiguousarray(packed.detach().cpu().numpy(), dtype=np.uint8)
+        sn = np.ascontiguousarray(scales.detach().cpu().to(torch.float32).numpy(), dtype=np.float32)
+        nslab = sn.shape[0]
+        slab_len = 2 * c.size // nslab
+        out = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.float64)
+        self.lib.gqa_oracle_dequant_int4(_ptr(c, _u8p), _ptr(sn, _fp), nslab, slab_len, _ptr(out, _dp))
+        return out
+
     # ---- cache append ---------------------------------------------------------------
     def append(self, case, k_new, v_new):
         """The caches of a decode case after storing the new token's key and value [B, G, D]
@@ -131,6 +163,10 @@ class Oracle:
                     i = b * G + g
                     kc.view(torch.uint8)[b, g, L - 1] = torch.from_numpy(self.quant_e4m3fn(kn[b, g], case.k_scale[i]))
                     vc.view(torch.uint8)[b, g, L - 1] = torch.from_numpy(self.quant_e4m3fn(vn[b, g], case.v_scale[i]))
+                elif case.kv_dtype == "int4":
+                    i = b * G + g
+                    kc[b, g, L - 1] = torch.from_numpy(self.quant_int4(kn[b, g], case.k_scale[i]))
+                    vc[b, g, L - 1] = torch.from_numpy(self.quant_int4(vn[b, g], case.v_scale[i]))
                 else:
                     kc[b, g, L - 1] = k_new[b, g].to(kc.dtype)
                     vc[b, g, L - 1] = v_new[b, g].to(vc.dtype)
@@ -156,6 +192,8 @@ class Oracle:
         if case.kv_dtype == "fp8_e4m3fn":
             return (self.dequant_e4m3fn(case.k_cache, case.k_scale),
                     self.dequant_e4m3fn(case.v_cache, case.v_scale))
+        if case.kv_dtype == "int4":
+            return self.dequant_int4(case.k_cache, case.k_scale), self.dequant_int4(case.v_cache, case.v_scale)
         return _f64(case.k_cache), _f64(case.v_cache)
 
     def decode_arrays(self, q, k_cache, v_cache, seq_lens, scale) -> np.ndarray:
@@ -311,5 +349,9 @@ def e4m3fn_value(code): return load().e4m3fn_value(code)
 def e4m3fn_encode(q): return load().e4m3fn_encode(q)
 def quant_e4m3fn(x, scale): return load().quant_e4m3fn(x, scale)
 def append(case, k_new, v_new): return load().append(case, k_new, v_new)
+def int4_value(u): return load().int4_value(u)
+def int4_encode(q): return load().int4_encode(q)
+def quant_int4(x, scale): return load().quant_int4(x, scale)
+def dequant_int4(packed, scales): return load().dequant_int4(packed, scales)
 def num_threads(): return load().num_threads()
 def set_num_threads(n): return load().set_num_threads(n)

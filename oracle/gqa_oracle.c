@@ -43,6 +43,12 @@
  *   (value 2^-6 * m/8); S.1111.111 is NaN and there are no infinities, so the
  *   largest finite magnitude is 2^8 * 1.75 = 448.
  *
+ *   INT4 KV storage (same page and section, which names 4-bit storage for K/V and gives
+ *   no format; this oracle's reading): each 4-bit field u in 0..15 stands for
+ *   (u - 8) * scale, one fp32 scale per (sequence, KV head); two fields per byte, the
+ *   low four bits holding the even head dim. A value x is stored as the integer nearest
+ *   to x / scale (the quotient in fp32, ties to even), clamped to -8 .. 7, plus 8.
+ *
  * Layouts (all contiguous, head dimension innermost):
  *   decode  q, out [B][H][D]; k_cache, v_cache [B][G][T_cap][D]; seq_lens [B]
  *   prefill q, out [B][H][T][D]; k, v [B][G][T][D]
@@ -337,5 +343,50 @@ void gqa_oracle_dequant_e4m3fn(const uint8_t *codes, const float *scales, long n
         long i;
         for (i = 0; i < slab_len; ++i)
             out[s * slab_len + i] = gqa_oracle_e4m3fn_value(codes[s * slab_len + i]) * sc;
+    }
+}
+
+/* INT4 field u (0..15) -> its value in units of the scale: u - 8. */
+int gqa_oracle_int4_value(int u) { return (u & 15) - 8; }
+
+/* Field for the fp32 quotient q: the nearest integer, ties to even, clamped to -8 .. 7,
+ * then + 8. NaN stores the field of 0 (8). */
+int gqa_oracle_int4_encode(float q)
+{
+    double x = (double)q, r, f;
+    if (isnan(x)) return 8;
+    r = floor(x);
+    f = x - r;
+    if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    if (r < -8.0) r = -8.0;
+    if (r > 7.0) r = 7.0;
+    return (int)r + 8;
+}
+
+/* Quantise n values (n even) to packed fields: byte i holds x[2i] (low) and x[2i+1] (high),
+ * each the field of x / scale, the quotient taken in fp32. */
+void gqa_oracle_quant_int4(const float *x, float scale, long n, uint8_t *packed)
+{
+    long i;
+    for (i = 0; i + 1 < n; i += 2) {
+        int lo = gqa_oracle_int4_encode(x[i] / scale), hi = gqa_oracle_int4_encode(x[i + 1] / scale);
+        packed[i / 2] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+/* Packed INT4 slabs -> float64 values: out[s][i] = (field i of slab s - 8) * scales[s];
+ * slab_len counts values (even). */
+void gqa_oracle_dequant_int4(const uint8_t *packed, const float *scales, long nslab, long slab_len, double *out)
+{
+    long s;
+#pragma omp parallel for schedule(static)
+    for (s = 0; s < nslab; ++s) {
+        double sc = (double)scales[s];
+        long i;
+        for (i = 0; i < slab_len; ++i) {
+            uint8_t byte = packed[(s * slab_len + i) / 2];
+            int u = (i & 1) ? (byte >> 4) : (byte & 15);
+            out[s * slab_len + i] = (double)gqa_oracle_int4_value(u) * sc;
+        }
     }
 }

@@ -374,8 +374,28 @@ def pin_chunk_short_cache(orc):
         assert np.array_equal(nc[:, :, i], orc.decode_arrays(q[:, :, i], k, v, lens, 0.5)), f"row {i}"
 
 
+def pin_int4_format(orc):
+    """INT4 fields: every field encodes back to itself, midpoints go to the even integer, values
+    saturate at -8 and 7, NaN stores zero; a hand-packed byte decodes low field first."""
+    for u in range(16):
+        assert orc.int4_value(u) == u - 8
+        assert orc.int4_encode(float(u - 8)) == u, f"field {u}"
+    for k in range(-8, 7):
+        even = k if k % 2 == 0 else k + 1
+        assert orc.int4_encode(k + 0.5) == even + 8, f"midpoint {k} + 1/2"
+        assert orc.int4_encode(np.nextafter(np.float32(k + 0.5), np.float32(-100))) == k + 8
+    assert orc.int4_encode(100.0) == 15 and orc.int4_encode(-100.0) == 0
+    assert orc.int4_encode(7.5) == 15 and orc.int4_encode(-8.5) == 0
+    assert orc.int4_encode(float("nan")) == 8
+    vals = orc.dequant_int4(torch.tensor([[0x1F, 0x80]], dtype=torch.uint8), torch.tensor([0.5]))
+    assert np.array_equal(vals, [[3.5, -3.5, -4.0, 0.0]]), vals
+    assert np.array_equal(orc.quant_int4(np.array([3.4, -3.6, -4.0, 0.2], dtype=np.float32), 0.5),
+                          np.array([0x1F, 0x80], dtype=np.uint8))
+
+
 ALL_PINS = [pin_hand_worked, pin_toy_three_ways, pin_sdpa_prefill, pin_sdpa_decode, pin_mha, pin_mqa,
             pin_group_materialise, pin_identical_keys_mean_v, pin_value_constant_per_head, pin_single_row,
             pin_shift_invariance, pin_permutation_invariance, pin_linear_and_convex,
             pin_incremental_decode_equals_prefill, pin_nan_padding, pin_length_readings, pin_e4m3fn_decoder,
-            pin_e4m3fn_encoder, pin_chunk_special_cases, pin_chunks_compose_prefill, pin_chunk_short_cache]
+            pin_e4m3fn_encoder, pin_chunk_special_cases, pin_chunks_compose_prefill, pin_chunk_short_cache,
+            pin_int4_format]

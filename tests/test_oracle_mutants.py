@@ -26,6 +26,10 @@ MUTANTS = [
      "codes[i] = gqa_oracle_e4m3fn_encode(x[i] * scale);"),
     ("fp8_sign_dropped", "return (uint8_t)(best | (neg << 7));", "return (uint8_t)best;"),
     ("chunk_offset_off_by_one", "long p = L - Tq + i;", "long p = L - Tq + i + 1;"),
+    ("int4_zero_point_7", "int gqa_oracle_int4_value(int u) { return (u & 15) - 8; }",
+     "int gqa_oracle_int4_value(int u) { return (u & 15) - 7; }"),
+    ("int4_nibble_order", "int u = (i & 1) ? (byte >> 4) : (byte & 15);", "int u = (i & 1) ? (byte & 15) : (byte >> 4);"),
+    ("int4_ties_to_odd", "(f == 0.5 && fmod(r, 2.0) != 0.0)", "(f == 0.5 && fmod(r, 2.0) == 0.0)"),
     ("chunk_not_causal_masks", "long n = causal ? (p + 1 < L ? p + 1 : L) : L;", "long n = p + 1 < L ? p + 1 : L;"),
 ]
 

@@ -36,6 +36,7 @@ import torch
 F32 = "f32"
 BF16 = "bf16"
 FP8 = "fp8_e4m3fn"
+INT4 = "int4"   # packed: [..., D/2] uint8, low four bits = even head dim, field u = code + 8
 
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn}
 FP8_MAX = 448.0
@@ -124,6 +125,31 @@ def quantize_fp8_slabs(x: torch.Tensor, seq_lens: torch.Tensor):
     return codes, scales
 
 
+INT4_MAX = 7.0
+
+
+def quantize_int4_slabs(x: torch.Tensor, seq_lens: torch.Tensor):
+    """Store float32 ``x`` [B, G, T_cap, D] as packed INT4 fields with one scale per (b, g):
+    scale = absmax of the slab's valid rows / 7, code = round-half-even(x / scale) clamped to
+    -8 .. 7, field = code + 8, two fields per byte (low four bits = even head dim). Padding
+    rows hold 0xFF (the largest value, 7 * scale: a kernel that reads them is off). Returns
+    (packed uint8 [B, G, T_cap, D/2], scales float32 [B*G])."""
+    B, G, T_cap, D = x.shape
+    assert D % 2 == 0
+    packed = torch.full((B, G, T_cap, D // 2), 0xFF, dtype=torch.uint8)
+    scales = torch.empty(B * G, dtype=torch.float32)
+    for b in range(B):
+        L = int(min(max(int(seq_lens[b]), 0), T_cap))
+        for g in range(G):
+            slab = x[b, g, :L]
+            amax = float(slab.abs().max()) if L > 0 else 0.0
+            s = float(torch.tensor(amax / INT4_MAX if amax > 0 else 1.0, dtype=torch.float32))
+            scales[b * G + g] = s
+            code = torch.round(slab / s).clamp(-8, 7).to(torch.int32) + 8
+            packed[b, g, :L] = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed, scales
+
+
 def make_decode(B, H, G, D, seq_lens, T_cap=None, q_dtype=BF16, kv_dtype=BF16, seed=0,
                 name="decode", scale=None, poison=True) -> DecodeCase:
     """Decode inputs. ``seq_lens`` is an int (same length for every sequence), a
@@ -149,6 +175,9 @@ def make_decode(B, H, G, D, seq_lens, T_cap=None, q_dtype=BF16, kv_dtype=BF16, s
     if kv_dtype == FP8:
         k_st, k_scale = quantize_fp8_slabs(k, lens)
         v_st, v_scale = quantize_fp8_slabs(v, lens)
+    elif kv_dtype == INT4:
+        k_st, k_scale = quantize_int4_slabs(k, lens)
+        v_st, v_scale = quantize_int4_slabs(v, lens)
     else:
         if poison:
             for b in range(B):
