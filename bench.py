@@ -8,7 +8,8 @@ workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H
 D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
 B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown", and so are the headline
 and fp8 decodes with the current token's KV-cache append done by the same call ("+append"),
-three decodes over a cache in shuffled 16-row pages ("_paged16"), and a prefill of the last
+three decodes over a cache in shuffled 16-row pages ("_paged16"), two decodes over INT4
+caches, and a prefill of the last
 512 positions of 4096-token sequences against the cache of the first 3584.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
@@ -98,14 +99,14 @@ def measured_traffic(workload: str):
 def decode_bytes(c: W.DecodeCase, append: bool = False) -> dict:
     """KV bytes = valid rows only: 2 (K and V) x sum_b L_b x G x D x element size. With a
     cache append, the new K/V rows are read (q's dtype) and written (cache dtype) once more."""
-    esz = {W.F32: 4, W.BF16: 2, W.FP8: 1}
+    esz = {W.F32: 4, W.BF16: 2, W.FP8: 1, W.INT4: 0.5}
     lens = c.seq_lens.clamp(0, c.T_cap).to(torch.int64)
-    kv = 2 * int(lens.sum()) * c.G * c.D * esz[c.kv_dtype]
+    kv = int(2 * int(lens.sum()) * c.G * c.D * esz[c.kv_dtype])
     qo = 2 * c.B * c.H * c.D * esz[c.q_dtype]
-    extra = 4 * c.B + (8 * c.B * c.G if c.kv_dtype == W.FP8 else 0)   # seq_lens (+ fp8 scales)
+    extra = 4 * c.B + (8 * c.B * c.G if c.kv_dtype in (W.FP8, W.INT4) else 0)   # seq_lens (+ scales)
     if append:
         n_rows = int(((c.seq_lens >= 1) & (c.seq_lens <= c.T_cap)).sum()) * c.G
-        extra += 2 * n_rows * c.D * (esz[c.q_dtype] + esz[c.kv_dtype])
+        extra += int(2 * n_rows * c.D * (esz[c.q_dtype] + esz[c.kv_dtype]))
     if isinstance(c, W.PagedDecodeCase):  # block-table entries of the pages holding valid rows
         extra += 4 * int(((lens + c.page_size - 1) // c.page_size).sum())
     return {"kv": kv, "total": kv + qo + extra}
@@ -410,6 +411,13 @@ def main():
             if W.WORKLOADS[name] is not W.causal_prefill_2048:
                 _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
                 breakdown[name + "+append"] = r
+        # INT4 caches (4-bit fields, one scale per sequence and KV head).
+        for wl in (W.mqa_int4_long_decode, W.llama70b_ragged_decode_int4):
+            ic = wl(0)
+            log(f"[bench] {ic.name}")
+            r = bench_decode(gqa, ic, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
+            log(f"[bench] {ic.name}: {json.dumps(r)}")
+            breakdown[ic.name] = r
         # Prefill of a 512-token chunk against a 3584-token cache.
         cc = W.chunked_prefill_512_of_4096(0)
         log(f"[bench] {cc.name}")

@@ -27,10 +27,10 @@ __all__ = ["decode", "decode_paged", "prefill", "prefill_cached", "decode_num_sp
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
 
 GQA_OK = 0
-DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3fn": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3fn": 2, "int4": 3}
 PATHS = {"auto": 0, "generic": 1, "valu": 2, "mfma": 3}
 LAYOUTS = {"auto": 0, "uniform": 1, "flat": 2}
-_TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
+_TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.uint8: 3}  # uint8 = packed INT4
 
 
 class GqaError(RuntimeError):
@@ -156,9 +156,9 @@ def _decode_opts(q, cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, l
     kv_code = _dtype_code(cache, "k_cache")
     o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
                  num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
-    if kv_code == DTYPES["fp8_e4m3fn"]:
+    if kv_code in (DTYPES["fp8_e4m3fn"], DTYPES["int4"]):
         if k_scale is None or v_scale is None:
-            raise ValueError("fp8 caches need k_scale and v_scale")
+            raise ValueError("fp8 and INT4 caches need k_scale and v_scale")
         for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
             _need_cuda(t, n)
             if t.dtype != torch.float32 or t.numel() != B * G:
@@ -200,6 +200,8 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
         raise ValueError("expected q [B,H,D] and k_cache, v_cache [B,G,T_cap,D]")
     B, H, D = q.shape
     Bk, G, T_cap, Dk = k_cache.shape
+    if k_cache.dtype == torch.uint8:  # packed INT4: two head dims per byte
+        Dk *= 2
     if Bk != B or Dk != D or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
         raise ValueError("shape mismatch between q, caches and seq_lens (int32 [B])")
     if k_cache.dtype != v_cache.dtype:
@@ -234,6 +236,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=Non
         raise ValueError("expected q [B,H,D], pools [num_pages,G,page_size,D] and block_table [B,pages_per_seq]")
     B, H, D = q.shape
     num_pages, G, page_size, Dk = k_pages.shape
+    if k_pages.dtype == torch.uint8:  # packed INT4
+        Dk *= 2
     Bt, pages_per_seq = block_table.shape
     if Bt != B or Dk != D or block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
             or seq_lens.numel() != B:

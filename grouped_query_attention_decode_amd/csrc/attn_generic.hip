@@ -1,4 +1,4 @@
-// Generic GQA attention kernel: any head dim 1..256, fp32 / bf16 / fp8-E4M3FN KV.
+// Generic GQA attention kernel: any head dim 1..256, fp32 / bf16 / fp8-E4M3FN / INT4 KV.
 //
 // Serves the shapes the vectorised kernels do not (tiny or odd head dims such as the
 // 12-dim, 4-head toy with D = 3) and is the family every fast kernel is cross-checked
@@ -98,18 +98,20 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, int 
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) acc[s] = 0.f;
 
+    // Element index of this slab's first value (packed INT4 holds two values per byte, so the
+    // offset is kept in elements and added to every index).
     const long slab = ((long)b * G + g) * (long)a.Tk * D;
-    const KT *kp = static_cast<const KT *>(a.k) + slab;
-    const KT *vp = static_cast<const KT *>(a.v) + slab;
-    const float ksc = KVT == DT_FP8 ? a.k_scale[bg] : 1.f;
-    const float vsc = KVT == DT_FP8 ? a.v_scale[bg] : 1.f;
+    const KT *kp = static_cast<const KT *>(a.k);
+    const KT *vp = static_cast<const KT *>(a.v);
+    const float ksc = KVT == DT_FP8 || KVT == DT_INT4 ? a.k_scale[bg] : 1.f;
+    const float vsc = KVT == DT_FP8 || KVT == DT_INT4 ? a.v_scale[bg] : 1.f;
 
     for (int t0 = kb; t0 < ke; t0 += kTileN) {
         const int n = ke - t0 < kTileN ? ke - t0 : kTileN;
         __syncthreads();  // previous tile fully consumed
         for (int e = tid; e < n * D; e += kThreads) {
-            k_s[e] = load_f32(kp, (long)t0 * D + e) * ksc;
-            v_s[e] = load_f32(vp, (long)t0 * D + e) * vsc;
+            k_s[e] = load_f32(kp, slab + (long)t0 * D + e) * ksc;
+            v_s[e] = load_f32(vp, slab + (long)t0 * D + e) * vsc;
         }
         __syncthreads();
         // Scores in the base-2 domain; masked or absent keys are -inf.
@@ -217,6 +219,8 @@ hipError_t launch_generic(const AttnArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((attn_generic_kernel<uint16_t, DT_BF16>), grid, block, 0, stream, a, hpw, tm);
     else if (a.q_dtype == DT_BF16 && a.kv_dtype == DT_FP8)
         hipLaunchKernelGGL((attn_generic_kernel<uint16_t, DT_FP8>), grid, block, 0, stream, a, hpw, tm);
+    else if (a.q_dtype == DT_BF16 && a.kv_dtype == DT_INT4)
+        hipLaunchKernelGGL((attn_generic_kernel<uint16_t, DT_INT4>), grid, block, 0, stream, a, hpw, tm);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -1,4 +1,4 @@
-// GQA decode on the matrix cores (bf16 or fp8-E4M3FN KV cache, D = 128, any R = H/G <= 64).
+// GQA decode on the matrix cores (bf16, fp8-E4M3FN or INT4 KV cache, D = 128, any R = H/G <= 64).
 //
 // Both contractions run as bf16 MFMA, even for narrow groups (R = 4), where most MFMA rows
 // are padding: a decode step is latency-bound per wave, and the matrix cores finish a block
@@ -24,7 +24,8 @@
 //   O^T (128 d x 16 heads) += V^T . P^T                          -- 16x16x32 bf16 MFMA
 //        V rows are loaded coalesced (4 rows of 256 bytes per wave instruction), written to
 //        a wave-private LDS tile, and read back transposed with ds_read_b64_tr_b16
-//        (ds_read_b64_tr_b8 + exact fp8->bf16 widening for fp8).
+//        (ds_read_b64_tr_b8 + exact fp8->bf16 widening for fp8; INT4 rows are widened to
+//        bf16 on their way into the tile, and K fields straight into the operands).
 // Tokens at or beyond the valid length are masked by index; their rows are never loaded
 // (the load index is clamped to the last valid row, and their probabilities are zero).
 // v_scale multiplies the output once, in the epilogue.
@@ -54,9 +55,34 @@ __device__ __forceinline__ int tau(int blk, int m) { return ((m >> 2) << 3) + (b
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | (r & 8) | ((r >> 4) & 1); }
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-template <bool FP8> struct Frag;
-template <> struct Frag<false> { i32x4_t k[8]; i32x4_t v[8]; };
-template <> struct Frag<true> { i32x4_t k[4]; i32x4_t v[4]; };
+// KV cache formats of this kernel. INT4 rows are widened to bf16 on the fly (see i4x8_to_bf16x8).
+enum : int { KV_BF16 = 0, KV_FP8 = 1, KV_I4 = 2 };
+
+// Bytes of one cache row in HBM, and of one V-tile row in LDS (INT4 V is widened to bf16).
+template <int KV> constexpr int kRowBytes = KV == KV_FP8 ? 128 : (KV == KV_I4 ? 64 : 256);
+template <int KV> constexpr int kLdsRowBytes = KV == KV_FP8 ? 128 : 256;
+
+// INT4 field u in a bf16 operand: bf16 bits 0x4300 | u are exactly 128 + u = 136 + code (bf16
+// has unit spacing in [128, 256)). The constant 136 is taken out of the products afterwards:
+// 136 * sum(q) from each score, 136 * sum(p) from each output.
+constexpr float kI4Offset = 136.f;
+
+// Eight INT4 fields (byte i: field 2i low, 2i+1 high) -> eight bf16 values 136 + code.
+__device__ __forceinline__ i32x4_t i4x8_to_bf16x8(int w) {
+    const uint32_t x = (uint32_t)w;
+    i32x4_t r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t t = (x >> (8 * m)) & 0xFFu;
+        r[m] = (int)(0x43004300u | (t & 0xFu) | ((t & 0xF0u) << 12));
+    }
+    return r;
+}
+
+template <int KV> struct Frag;
+template <> struct Frag<KV_BF16> { i32x4_t k[8]; i32x4_t v[8]; };
+template <> struct Frag<KV_FP8> { i32x4_t k[4]; i32x4_t v[4]; };
+template <> struct Frag<KV_I4> { i32x4_t k[2]; i32x4_t v[2]; };
 
 typedef const __attribute__((address_space(4))) int32_t cint32_t;
 
@@ -103,16 +129,20 @@ __device__ __forceinline__ long row_off(const KvSrc &s, PageOffs p, int t0, int 
     }
 }
 
-template <bool FP8, bool PAGED>
-__device__ __forceinline__ void load_block(Frag<FP8> &f, const KvSrc &src, PageOffs pg, int t0, int ke,
+template <int KV, bool PAGED>
+__device__ __forceinline__ void load_block(Frag<KV> &f, const KvSrc &src, PageOffs pg, int t0, int ke,
                                            int lane) {
-    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int RB = kRowBytes<KV>;
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         int row = t0 + tau(blk, lane & 15);
         row = row < ke ? row : ke - 1;
         const char *kr = src.k + row_off<PAGED, RB>(src, pg, t0, row);
-        if constexpr (FP8) {
+        if constexpr (I4) {
+            // 32 INT4 fields per lane: head dims 32*(l/16) .. +31, eight per k-step.
+            f.k[blk] = *(const i32x4_t *)(kr + 16 * (lane >> 4));
+        } else if constexpr (FP8) {
             // 16 fp8 per lane: head dims 64p + 16*(l/16) .. +15 feed k-steps 2p and 2p+1.
 #pragma unroll
             for (int p = 0; p < 2; ++p) f.k[blk * 2 + p] = *(const i32x4_t *)(kr + 64 * p + 16 * (lane >> 4));
@@ -121,7 +151,15 @@ __device__ __forceinline__ void load_block(Frag<FP8> &f, const KvSrc &src, PageO
             for (int kk = 0; kk < 4; ++kk) f.k[blk * 4 + kk] = *(const i32x4_t *)(kr + 64 * kk + 16 * (lane >> 4));
         }
     }
-    if constexpr (FP8) {
+    if constexpr (I4) {
+        // 16 rows of 64 bytes per wave instruction: lane l reads head dims 32*(l%4) .. +31.
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int row = t0 + 16 * i + (lane >> 2);
+            row = row < ke ? row : ke - 1;
+            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 3));
+        }
+    } else if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int row = t0 + 8 * i + (lane >> 3);
@@ -140,16 +178,20 @@ __device__ __forceinline__ void load_block(Frag<FP8> &f, const KvSrc &src, PageO
 
 // Q^T as the B operand: lane l holds Q[head 16*hb + l%16][dk .. dk+7] for k-step kk. Padded
 // heads (index >= R) load head R-1 so that the loads stay unconditional; attend() zeroes them.
-template <int NHB, bool FP8>
+template <int NHB, int KV>
 __device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp, int R, int lane) {
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         const int h = hb * 16 + (lane & 15);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             // k-step kk covers head dims dk(kk) .. +7 of this lane; fp8 pairs the steps so
-            // that one 16-byte K load serves two of them (the same order on both operands).
-            const int dk = FP8 ? 64 * (kk >> 1) + 16 * (lane >> 4) + 8 * (kk & 1) : 32 * kk + 8 * (lane >> 4);
+            // that one 16-byte K load serves two of them, INT4 lets one serve all four (the
+            // same order on both operands).
+            const int dk = I4    ? 32 * (lane >> 4) + 8 * kk
+                           : FP8 ? 64 * (kk >> 1) + 16 * (lane >> 4) + 8 * (kk & 1)
+                                 : 32 * kk + 8 * (lane >> 4);
             qT[hb][kk] = *(const i32x4_t *)(qp + (long)(h < R ? h : R - 1) * kD + dk);
         }
     }
@@ -161,10 +203,11 @@ __device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp
 // operand layout and in the V row layout alike -- put the new chunk (quantised for an fp8
 // cache) in its place and store it to the cache, so the row is written once and attended to
 // with exactly the bytes stored.
-template <bool FP8, bool PAGED>
-__device__ __forceinline__ void append_row(Frag<FP8> &f, const AttnArgs &a, int bg, const KvSrc &src, int t0, int r,
+template <int KV, bool PAGED>
+__device__ __forceinline__ void append_row(Frag<KV> &f, const AttnArgs &a, int bg, const KvSrc &src, int t0, int r,
                                            int lane) {
-    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int RB = kRowBytes<KV>;
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (long)bg * kD;
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (long)bg * kD;
     const long ro = row_off<PAGED, RB>(src, fetch_pages<PAGED>(src, t0), t0, r);
@@ -173,7 +216,10 @@ __device__ __forceinline__ void append_row(Frag<FP8> &f, const AttnArgs &a, int 
     const int rb = r - t0;  // row in the block, 0..31
     // Registers are chosen by per-lane predicates over compile-time indices, so that the
     // fragment stays in registers.
-    if constexpr (FP8) {
+    if constexpr (I4) {
+        // INT4 caches are appended by the copy kernel before the attention, never here.
+        (void)f; (void)kr; (void)vr; (void)rb; (void)kn; (void)vn; (void)lane;
+    } else if constexpr (FP8) {
         // The wave quantises the 256 new values once, four per lane (K dims 4l .. 4l+3 in lanes
         // 0-31, V dims in lanes 32-63), and each lane gathers the four words of its chunks.
         const int hl = lane & 31;
@@ -234,14 +280,15 @@ struct PieceOut {
 // Attention of query heads head0 .. head0+R-1 over key rows kb .. ke-1 of one (sequence, KV
 // head), by the whole workgroup: each wave streams blocks kb + 32 (wave + 4 i), then the four
 // waves merge. The caller has requested q (qT) and this wave's first block (nxt) already.
-template <int NHB, bool FP8, bool PAGED>
+template <int NHB, int KV, bool PAGED>
 __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w)[16 * NHB], float (*l_w)[16 * NHB],
                                        int lane, int wave, long head0, int R, int bg, int kb, int ke, PieceOut po,
-                                       i32x4_t (&qT)[NHB][4], Frag<FP8> &nxt, const KvSrc &src, float c,
+                                       i32x4_t (&qT)[NHB][4], Frag<KV> &nxt, const KvSrc &src, float c,
                                        float vscale) {
-    constexpr int RB = FP8 ? 128 : 256;
-    constexpr int VT = kBlockT * RB;  // V tile bytes per wave
-    constexpr int HP = 16 * NHB;      // heads padded to MFMA blocks
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
+    constexpr int RBL = kLdsRowBytes<KV>;  // V-tile row bytes in LDS
+    constexpr int VT = kBlockT * RBL;      // V tile bytes per wave
+    constexpr int HP = 16 * NHB;           // heads padded to MFMA blocks
     const int S = a.num_splits;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -249,13 +296,34 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qT[hb][kk] = i32x4_t{0, 0, 0, 0};
     char *vt = lds + wave * VT;
+    // INT4: 136 * sum_d q[h][d] for the lane's head, to take out of every score.
+    float qoff[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        qoff[hb] = 0.f;
+        if constexpr (I4) {
+            float sum = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = (uint32_t)qT[hb][kk][e];
+                    sum += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+                }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            qoff[hb] = kI4Offset * sum;
+        }
+    }
 
     f32x4_t o[NHB][8];
     float m[NHB], lsum[NHB];
+    float lb[NHB];  // INT4: running sum of the bf16-rounded probabilities the P.V product used
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         m[hb] = -INFINITY;
         lsum[hb] = 0.f;
+        lb[hb] = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) o[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -267,12 +335,13 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 
     // One 32-token block: `slot` holds its K/V rows (requested earlier) and is refilled with
     // the block `dist` rows ahead (dist = 0: the wave's last block, nothing to refill).
-    auto step = [&](Frag<FP8> &slot, int t0, int dist) {
-        Frag<FP8> cur = slot;
+    auto step = [&](Frag<KV> &slot, int t0, int dist) {
+        Frag<KV> cur = slot;
         // Rows at or past the end may hold anything, NaN included (a first block requested
         // before the length was known reads up to the allocation). Their scores are masked by
-        // index below; zero their values so that the zero probabilities stay exact.
-        if (t0 + kBlockT > ke) {
+        // index below; zero their values so that the zero probabilities stay exact. (Every
+        // INT4 field is finite: nothing to clear.)
+        if (!I4 && t0 + kBlockT > ke) {
             if constexpr (FP8) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -284,25 +353,34 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             }
         }
         // V tile -> LDS (row-major, swizzled 16-byte chunks) first, so the V registers are
-        // free again before the next block's loads are issued.
-        if constexpr (FP8) {
+        // free again before the next block's loads are issued. INT4 rows are widened to the
+        // bf16 tile layout on the way (four 8-dim chunks per lane).
+        if constexpr (I4) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 16 * i + (lane >> 2);
+#pragma unroll
+                for (int mq = 0; mq < 4; ++mq)
+                    *(i32x4_t *)(vt + r * RBL + 16 * ((4 * (lane & 3) + mq) ^ swz16(r))) = i4x8_to_bf16x8(cur.v[i][mq]);
+            }
+        } else if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 8 * i + (lane >> 3);
-                *(i32x4_t *)(vt + r * RB + 16 * ((lane & 7) ^ swz8(r))) = cur.v[i];
+                *(i32x4_t *)(vt + r * RBL + 16 * ((lane & 7) ^ swz8(r))) = cur.v[i];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = 4 * i + (lane >> 4);
-                *(i32x4_t *)(vt + r * RB + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
+                *(i32x4_t *)(vt + r * RBL + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
             }
         }
         // Prefetch this slot's next block (dist rows ahead, always inside the range) before this
         // block's work; the barrier keeps the scheduler from sinking it next to its use --
         // otherwise every block waits out a full memory latency.
         if (dist > 0) {
-            load_block<FP8, PAGED>(slot, src, pgn, t0 + dist, ke, lane);
+            load_block<KV, PAGED>(slot, src, pgn, t0 + dist, ke, lane);
             if constexpr (PAGED) pgn = fetch_pages<PAGED>(src, t0 + 2 * dist);  // for the next prefetch
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -314,7 +392,9 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             i32x4_t ka[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                if constexpr (FP8) {
+                if constexpr (I4) {
+                    ka[kk] = i4x8_to_bf16x8(cur.k[blk][kk]);
+                } else if constexpr (FP8) {
                     const i32x4_t w = cur.k[blk * 2 + (kk >> 1)];
                     ka[kk] = e4m3x8_to_bf16x8((kk & 1) ? i32x2_t{w[2], w[3]} : i32x2_t{w[0], w[1]});
                 } else {
@@ -343,7 +423,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = tl + 4 * blk + i;
-                    const float v = t < ke ? s[hb][blk][i] * c : -INFINITY;
+                    const float v = t < ke ? (s[hb][blk][i] - qoff[hb]) * c : -INFINITY;
                     x[blk * 4 + i] = v;
                     bm = fmaxf(bm, v);
                 }
@@ -370,6 +450,13 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             pb[hb][1] = pack_bf16_rne(x[2], x[3]);
             pb[hb][2] = pack_bf16_rne(x[4], x[5]);
             pb[hb][3] = pack_bf16_rne(x[6], x[7]);
+            if constexpr (I4) {
+                float sb = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    sb += __uint_as_float((uint32_t)pb[hb][w] << 16) + __uint_as_float((uint32_t)pb[hb][w] & 0xffff0000u);
+                lb[hb] = lb[hb] * alpha + sb;
+            }
         }
 
         // O^T += V^T . P^T, 16 head dims per MFMA.
@@ -379,14 +466,14 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             i32x4_t va;
             if constexpr (FP8) {
                 const int r = 8 * grp + (j >> 1);
-                const i32x2_t codes = lds_read_tr8(vt + r * RB + 16 * (nb ^ swz8(r)) + 8 * (j & 1));
+                const i32x2_t codes = lds_read_tr8(vt + r * RBL + 16 * (nb ^ swz8(r)) + 8 * (j & 1));
                 va = e4m3x8_to_bf16x8(codes);
             } else {
                 const int r0 = 8 * grp + (j >> 2);
                 const int r1 = r0 + 4;
                 const int cc = 2 * nb + ((j & 3) >> 1);
-                const i32x2_t lo = lds_read_tr16(vt + r0 * RB + 16 * (cc ^ swz16(r0)) + 8 * (j & 1));
-                const i32x2_t hi = lds_read_tr16(vt + r1 * RB + 16 * (cc ^ swz16(r1)) + 8 * (j & 1));
+                const i32x2_t lo = lds_read_tr16(vt + r0 * RBL + 16 * (cc ^ swz16(r0)) + 8 * (j & 1));
+                const i32x2_t hi = lds_read_tr16(vt + r1 * RBL + 16 * (cc ^ swz16(r1)) + 8 * (j & 1));
                 va = i32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
@@ -399,8 +486,24 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         // of a cache append, and code for that kept out of the loop costs it no registers.
         const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
         for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep);
-        if (po.append && tl + kBlockT >= ke) append_row<FP8, PAGED>(nxt, a, bg, src, tl, ke - 1, lane);
+        if (po.append && tl + kBlockT >= ke) append_row<KV, PAGED>(nxt, a, bg, src, tl, ke - 1, lane);
         step(nxt, tl, 0);
+    }
+    if constexpr (I4) {
+        // Take 136 * sum(p) out of every output: o held sum_t p_t (136 + code_t) v_scale-free.
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            lb[hb] += __shfl_xor(lb[hb], 16);
+            lb[hb] += __shfl_xor(lb[hb], 32);
+            const float corr = kI4Offset * lb[hb];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                o[hb][nb][0] -= corr;
+                o[hb][nb][1] -= corr;
+                o[hb][nb][2] -= corr;
+                o[hb][nb][3] -= corr;
+            }
+        }
     }
 
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
@@ -493,11 +596,13 @@ __device__ __forceinline__ KvSrc kv_src(const AttnArgs &a, int b, int g, int bg)
 
 // Uniform layout: workgroup = (key range `split`, sequence b, KV head g), ranges of split_len
 // keys. Split-major order: the blocks resident on one CU at once are far apart in the grid.
-template <int NHB, bool FP8, bool PAGED>
+template <int NHB, int KV, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
-    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int RB = kRowBytes<KV>;
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RB : kWaves * HP * kDP * 4;
+    constexpr int RBL = kLdsRowBytes<KV>;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RBL > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RBL : kWaves * HP * kDP * 4;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
 
@@ -516,13 +621,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     // block's rows are clamped to the allocation), so they are requested before it and share
     // its round trip.
     i32x4_t qT[NHB][4];
-    load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
-    const float kscale = FP8 ? a.k_scale[bg] : 1.f;
-    const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+    load_q<NHB, KV>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
+    const float kscale = FP8 || I4 ? a.k_scale[bg] : 1.f;
+    const float vscale = FP8 || I4 ? a.v_scale[bg] : 1.f;
     const KvSrc src = kv_src<PAGED, RB>(a, b, g, bg);
-    Frag<FP8> nxt;
+    Frag<KV> nxt;
     if (kb + wave * kBlockT < a.Tk)
-        load_block<FP8, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, a.Tk, lane);
+        load_block<KV, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, a.Tk, lane);
 
     const int Lraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     const int L = clamp_len(Lraw, a.Tk);
@@ -548,18 +653,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
     // With the in-kernel merge, a sequence whose keys all fall in this range needs no merge.
     po.direct = S == 1 || (a.fuse_combine && po.n_slots == 1);
     po.append = a.k_new && ke == L && Lraw == L;  // Lraw in 1..T_cap: the row exists
-    attend<NHB, FP8, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
+    attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
                             a.scale_log2 * kscale, vscale);
 }
 
 // Flat layout (splitkv.h): workgroup w streams rows [w C, (w + 1) C) of the concatenated
 // segments, piece by piece. Every workgroup gets the same number of rows, whatever the mix of
 // sequence lengths.
-template <int NHB, bool FP8, bool PAGED>
+template <int NHB, int KV, bool PAGED>
 __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_kernel(AttnArgs a) {
-    constexpr int RB = FP8 ? 128 : 256;
+    constexpr int RB = kRowBytes<KV>;
+    constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RB > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RB : kWaves * HP * kDP * 4;
+    constexpr int RBL = kLdsRowBytes<KV>;
+    constexpr int LDS_BYTES = kWaves * kBlockT * RBL > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RBL : kWaves * HP * kDP * 4;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
     __shared__ int lay_s[4];
@@ -634,52 +741,58 @@ __global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_k
         po.append = a.k_new && ke == Tb && Tbraw == Tb;
 
         i32x4_t qT[NHB][4];
-        load_q<NHB, FP8>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
-        const float kscale = FP8 ? a.k_scale[bg] : 1.f;
-        const float vscale = FP8 ? a.v_scale[bg] : 1.f;
+        load_q<NHB, KV>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
+        const float kscale = FP8 || I4 ? a.k_scale[bg] : 1.f;
+        const float vscale = FP8 || I4 ? a.v_scale[bg] : 1.f;
         const KvSrc src = kv_src<PAGED, RB>(a, b, g, bg);
-        Frag<FP8> nxt;
+        Frag<KV> nxt;
         if (kb + wave * kBlockT < ke)
-            load_block<FP8, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, ke, lane);
-        attend<NHB, FP8, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
+            load_block<KV, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, ke, lane);
+        attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
                          a.scale_log2 * kscale, vscale);
         __syncthreads();  // the next piece reuses the LDS tiles
         x = s0 + ke;
     }
 }
 
-template <int NHB, bool FP8, bool PAGED>
+template <int NHB, int KV, bool PAGED>
 hipError_t launch_nhb(const AttnArgs &a, hipStream_t stream) {
     if (a.flat) {
-        hipLaunchKernelGGL((decode_mfma_flat_kernel<NHB, FP8, PAGED>), dim3((unsigned)a.flat_nw), dim3(kThreads), 0,
+        hipLaunchKernelGGL((decode_mfma_flat_kernel<NHB, KV, PAGED>), dim3((unsigned)a.flat_nw), dim3(kThreads), 0,
                            stream, a);
     } else {
         dim3 grid((unsigned)(a.B * a.G * a.num_splits));
-        hipLaunchKernelGGL((decode_mfma_kernel<NHB, FP8, PAGED>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<NHB, KV, PAGED>), grid, dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
 
-template <bool FP8, bool PAGED>
+template <int KV, bool PAGED>
 hipError_t launch_kv(const AttnArgs &a, hipStream_t stream) {
     const int R = a.H / a.G;
-    if (R <= 16) return launch_nhb<1, FP8, PAGED>(a, stream);
-    if (R <= 32) return launch_nhb<2, FP8, PAGED>(a, stream);
-    return launch_nhb<4, FP8, PAGED>(a, stream);
+    if (R <= 16) return launch_nhb<1, KV, PAGED>(a, stream);
+    if (R <= 32) return launch_nhb<2, KV, PAGED>(a, stream);
+    return launch_nhb<4, KV, PAGED>(a, stream);
 }
 
 }  // namespace
 
 bool decode_mfma_supports(const AttnArgs &a) {
-    return a.decode && a.D == kD && a.q_dtype == DT_BF16 && (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_FP8) &&
+    return a.decode && a.D == kD && a.q_dtype == DT_BF16 &&
+           (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_FP8 || a.kv_dtype == DT_INT4) &&
            a.H / a.G <= 64;
 }
 
 hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream) {
     if (!decode_mfma_supports(a)) return hipErrorInvalidValue;
-    if (a.block_table)
-        return a.kv_dtype == DT_FP8 ? launch_kv<true, true>(a, stream) : launch_kv<false, true>(a, stream);
-    return a.kv_dtype == DT_FP8 ? launch_kv<true, false>(a, stream) : launch_kv<false, false>(a, stream);
+    if (a.block_table) {
+        if (a.kv_dtype == DT_FP8) return launch_kv<KV_FP8, true>(a, stream);
+        if (a.kv_dtype == DT_INT4) return launch_kv<KV_I4, true>(a, stream);
+        return launch_kv<KV_BF16, true>(a, stream);
+    }
+    if (a.kv_dtype == DT_FP8) return launch_kv<KV_FP8, false>(a, stream);
+    if (a.kv_dtype == DT_INT4) return launch_kv<KV_I4, false>(a, stream);
+    return launch_kv<KV_BF16, false>(a, stream);
 }
 
 }  // namespace gqa

@@ -31,10 +31,16 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
     return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));  // rebias 7 -> 127
 }
 
+// Two INT4 fields in one byte (low four bits: the even element); field u stands for u - 8.
+struct I4x2 {
+    uint8_t b;
+};
+
 template <int KVT> struct KvElem;
 template <> struct KvElem<0> { using T = float; };
 template <> struct KvElem<1> { using T = uint16_t; };
 template <> struct KvElem<2> { using T = uint8_t; };
+template <> struct KvElem<3> { using T = I4x2; };
 
 // Cache append for fp8 slabs with a fixed scale: the E4M3FN code of the fp32 quotient x / scale,
 // magnitudes beyond the largest code (448) saturated, NaN to the NaN code 0x7F; the hardware
@@ -54,6 +60,19 @@ __device__ __forceinline__ uint32_t quant_e4m3fn_x4(float x0, float x1, float x2
 __device__ __forceinline__ float load_f32(const float *p, long i) { return p[i]; }
 __device__ __forceinline__ float load_f32(const uint16_t *p, long i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float load_f32(const uint8_t *p, long i) { return e4m3fn_to_f32(p[i]); }
+// Element i of a packed INT4 array (in units of its scale).
+__device__ __forceinline__ float load_f32(const I4x2 *p, long i) {
+    const uint32_t byte = p[i >> 1].b;
+    return (float)((int)((i & 1) ? byte >> 4 : byte & 15u) - 8);
+}
+
+// INT4 field of the fp32 quotient x / scale: nearest integer, ties to even (the default
+// rounding of rintf), clamped to -8 .. 7, plus 8; NaN stores the field of 0.
+__device__ __forceinline__ uint32_t quant_int4(float x, float scale) {
+    const float q = x / scale;
+    if (q != q) return 8u;
+    return (uint32_t)((int)fminf(fmaxf(rintf(q), -8.f), 7.f) + 8);
+}
 
 __device__ __forceinline__ void store_f32(float *p, long i, float x) { p[i] = x; }
 __device__ __forceinline__ void store_f32(uint16_t *p, long i, float x) { p[i] = f32_to_bf16(x); }

@@ -22,9 +22,10 @@ constexpr int kMaxSplitsAbi = 1024;
 constexpr int kNumDevicesMax = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1; }
+// Bytes per KV row of D values (INT4 packs two values per byte).
+long row_bytes(int dt, long D) { return dt == DT_F32 ? 4 * D : dt == DT_BF16 ? 2 * D : dt == DT_FP8 ? D : (D + 1) / 2; }
 
-bool valid_dtype(int dt) { return dt == DT_F32 || dt == DT_BF16 || dt == DT_FP8; }
+bool valid_dtype(int dt) { return dt == DT_F32 || dt == DT_BF16 || dt == DT_FP8 || dt == DT_INT4; }
 
 // Copy the caller's options over defaults, honouring struct_size (older, shorter
 // layouts keep the defaults for the fields they do not have).
@@ -46,7 +47,7 @@ int auto_splits(long B, long H, long G, long D, long T_cap, int kv_dtype) {
     const long R = H / G;
     const long units = B * G;
     const long target = 512;
-    long min_len = (8L * R * (D + 2) * 4 * 2) / (2L * D * elem_bytes(kv_dtype));
+    long min_len = (8L * R * (D + 2) * 4 * 2) / (2L * row_bytes(kv_dtype, D));
     if (min_len < 64) min_len = 64;
     long by_len = (T_cap + min_len - 1) / min_len;
     long by_units = (target + units - 1) / units;
@@ -146,7 +147,8 @@ DecodePlan plan_decode(int B, int H, int G, int D, int T_cap, int kv_dtype, int 
 // AUTO resolves to the matrix-core family wherever it applies: head dim 128 with a bf16 or fp8
 // cache (the cache type fixes q's: bf16), at most 64 query heads per KV head.
 int auto_path(int H, int G, int D, int kv_dtype) {
-    if (D == 128 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && H / G <= 64) return GQA_PATH_MFMA;
+    if (D == 128 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8 || kv_dtype == DT_INT4) && H / G <= 64)
+        return GQA_PATH_MFMA;
     return GQA_PATH_GENERIC;
 }
 
@@ -268,16 +270,19 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
     const bool pair_ok = (o.q_dtype == DT_F32 && o.kv_dtype == DT_F32) ||
                          (o.q_dtype == DT_BF16 && o.kv_dtype == DT_BF16) ||
-                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8);
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8) ||
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_INT4);
     if (!pair_ok) return GQA_ERR_UNSUPPORTED;
-    if (o.kv_dtype == DT_FP8 && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+    const bool scaled = o.kv_dtype == DT_FP8 || o.kv_dtype == DT_INT4;
+    if (scaled && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+    if (o.kv_dtype == DT_INT4 && D % 2 != 0) return GQA_ERR_UNSUPPORTED;  // whole bytes per row
     if ((o.k_new == nullptr) != (o.v_new == nullptr)) return GQA_ERR_INVALID_ARG;
 
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.seq_lens = seq_lens;
-    a.k_scale = o.kv_dtype == DT_FP8 ? o.k_scale : nullptr;
-    a.v_scale = o.kv_dtype == DT_FP8 ? o.v_scale : nullptr;
+    a.k_scale = scaled ? o.k_scale : nullptr;
+    a.v_scale = scaled ? o.v_scale : nullptr;
     a.B = B; a.H = H; a.G = G; a.D = D;
     a.Tq = 1; a.Tk = o.kv_capacity;
     a.causal = 0; a.decode = 1;
@@ -335,7 +340,8 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     if (o.k_new) {
         // The matrix-core kernel stores the new row itself, from the registers it attends with
         // (its 16-byte loads need 16-byte aligned rows); every other case copies it first.
-        const bool fused = path == GQA_PATH_MFMA && ((uintptr_t)o.k_new % 16) == 0 && ((uintptr_t)o.v_new % 16) == 0;
+        const bool fused = path == GQA_PATH_MFMA && o.kv_dtype != DT_INT4 && ((uintptr_t)o.k_new % 16) == 0 &&
+                           ((uintptr_t)o.v_new % 16) == 0;
         a.k_new = o.k_new;
         a.v_new = o.v_new;
         if (!fused) {
@@ -388,7 +394,7 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
     if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
     if (o.path < GQA_PATH_AUTO || o.path > GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
     if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
-    if (o.q_dtype != o.kv_dtype || o.q_dtype == DT_FP8) return GQA_ERR_UNSUPPORTED;
+    if (o.q_dtype != o.kv_dtype || o.q_dtype == DT_FP8 || o.q_dtype == DT_INT4) return GQA_ERR_UNSUPPORTED;
 
     AttnArgs a;
     memset(&a, 0, sizeof(a));

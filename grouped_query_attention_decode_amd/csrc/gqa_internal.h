@@ -6,7 +6,7 @@
 
 namespace gqa {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT4 = 3 };
 
 // Everything one attention launch needs. Pointers are device pointers.
 struct AttnArgs {

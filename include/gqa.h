@@ -62,7 +62,13 @@ typedef enum gqa_dtype {
      * stored value stands for code * scale with one fp32 scale per (sequence, KV
      * head) ["GQA revolution: how xformers speeds up LLM inference", section on
      * mixed-precision KV storage]. */
-    GQA_DTYPE_FP8_E4M3FN = 2
+    GQA_DTYPE_FP8_E4M3FN = 2,
+    /* 4-bit integer KV cache only: rows of D/2 bytes, byte i holding head dims 2i (low four
+     * bits) and 2i+1 (high four bits); a field u in 0..15 stands for (u - 8) * scale with one
+     * fp32 scale per (sequence, KV head), as for fp8. ["GQA revolution ...", section on
+     * mixed-precision KV storage, names 4-bit KV storage and no layout; this is the library's
+     * reading.] D must be even. */
+    GQA_DTYPE_INT4 = 3
 } gqa_dtype;
 
 /* Kernel family for decode. AUTO takes MFMA wherever it applies and GENERIC otherwise;
@@ -71,7 +77,7 @@ typedef enum gqa_path {
     GQA_PATH_AUTO = 0,
     GQA_PATH_GENERIC = 1,  /* any head dim 1..256, any supported dtype pair */
     GQA_PATH_VALU = 2,     /* vector-ALU dot products; bf16 KV, D = 128 */
-    GQA_PATH_MFMA = 3      /* matrix cores; bf16 or fp8 KV, bf16 q, D = 128 */
+    GQA_PATH_MFMA = 3      /* matrix cores; bf16, fp8 or INT4 KV, bf16 q, D = 128 */
 } gqa_path;
 
 /* Decode work layout. UNIFORM cuts every (sequence, KV head) into the same number of key
@@ -95,8 +101,8 @@ typedef struct gqa_opts {
     int32_t num_splits;     /* decode: KV splits per (sequence, KV head); 0 = choose */
     int32_t path;           /* gqa_path (default AUTO) */
     int32_t layout;         /* decode: gqa_layout (default AUTO); FLAT excludes num_splits > 0 */
-    const float *k_scale;   /* fp8 KV: device fp32 [B*G], index b*G + g; else NULL */
-    const float *v_scale;   /* fp8 KV: device fp32 [B*G]; else NULL */
+    const float *k_scale;   /* fp8 / INT4 KV: device fp32 [B*G], index b*G + g; else NULL */
+    const float *v_scale;   /* fp8 / INT4 KV: device fp32 [B*G]; else NULL */
     void *workspace;        /* device scratch for split partials, or NULL */
     size_t workspace_bytes; /* size of `workspace` */
     const void *k_new;      /* decode: the current token's key [B, G, D] (q's dtype) to append, or NULL */
@@ -114,6 +120,7 @@ void gqa_opts_init(gqa_opts *opts);
  *
  *   q        [B, H, D]            q_dtype, the current token's query heads
  *   k_cache  [B, G, T_cap, D]     kv_dtype, head dim innermost, T_cap = opts->kv_capacity
+ *                                 (INT4: [B, G, T_cap, D/2] bytes)
  *   v_cache  [B, G, T_cap, D]     kv_dtype
  *   seq_lens [B] int32 (device)   valid rows of sequence b, current token included
  *   out      [B, H, D]            q_dtype
@@ -148,8 +155,10 @@ void gqa_opts_init(gqa_opts *opts);
  * family writes the row inside the attention kernel; the other families run a small copy
  * kernel first.
  *
- * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
- * opts is required (it carries kv_capacity). D in 1..256.
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN), (BF16, INT4).
+ * opts is required (it carries kv_capacity). D in 1..256 (even for INT4). An INT4 append
+ * stores the nearest integer to k_new / k_scale (ties to even) clamped to -8 .. 7, by a copy
+ * kernel before the attention.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *seq_lens, void *out, int B, int H, int G, int D,
@@ -176,7 +185,7 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
  * Every option of gqa_decode applies (dtypes, fp8 scales per (sequence, KV head), workspace
  * of gqa_decode_workspace_size() for kv_capacity = pages_per_seq * page_size, layout, cache
  * append through opts->k_new / v_new, which writes the row's page). Kernel family: matrix
- * cores only (bf16 q with a bf16 or fp8 cache, D = 128); other paths and dtypes return
+ * cores only (bf16 q with a bf16, fp8 or INT4 cache, D = 128); other paths and dtypes return
  * GQA_ERR_UNSUPPORTED.
  */
 gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,

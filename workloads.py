@@ -397,6 +397,17 @@ def mqa_fp8_long_decode(seed=0) -> DecodeCase:
                        name="mqa_fp8_decode_B8_L32768")
 
 
+def mqa_int4_long_decode(seed=0) -> DecodeCase:
+    """The long-context MQA decode with an INT4 cache: B8 H32 G1 D128, 32768 tokens."""
+    return make_decode(8, 32, 1, 128, 32768, T_cap=32768, kv_dtype=INT4, seed=seed, name="mqa_int4_decode_B8_L32768")
+
+
+def llama70b_ragged_decode_int4(seed=0) -> DecodeCase:
+    """The ragged Llama-2-70B-shaped decode with an INT4 cache."""
+    return make_decode(16, 64, 8, 128, "uniform:1024:4096", T_cap=4096, kv_dtype=INT4, seed=seed,
+                       name="llama70b_gqa8_decode_B16_ragged_int4")
+
+
 def chunked_prefill_512_of_4096(seed=0) -> ChunkCase:
     """Chunked prefill: B4 H32 G8 D128, the last 512 positions of 4096-token sequences against
     the cache holding the first 3584 (and the chunk's own rows), causal, bf16."""
