@@ -597,7 +597,10 @@ __device__ __forceinline__ KvSrc kv_src(const AttnArgs &a, int b, int g, int bg)
 // Uniform layout: workgroup = (key range `split`, sequence b, KV head g), ranges of split_len
 // keys. Split-major order: the blocks resident on one CU at once are far apart in the grid.
 template <int NHB, int KV, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(AttnArgs a) {
+// Two workgroups per CU for up to 32 heads per KV head (the register budget then keeps the
+// accumulators in VGPRs without spilling): a wave's block is latency-bound, and a second
+// workgroup hides it (measured: fp8 MQA decode, R = 32, -9 %; Llama-7B decode -2 %).
+__global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel(AttnArgs a) {
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
