@@ -664,7 +664,10 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
 // segments, piece by piece. Every workgroup gets the same number of rows, whatever the mix of
 // sequence lengths.
 template <int NHB, int KV, bool PAGED>
-__global__ __launch_bounds__(kThreads, NHB == 1 ? 2 : 1) void decode_mfma_flat_kernel(AttnArgs a) {
+// Two workgroups per CU where the registers allow it without spills (R <= 16; R <= 32 for
+// the 8- and 4-bit caches): ragged fp8 MQA batch (R = 32) -3 %.
+__global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ? 2 : 1) void decode_mfma_flat_kernel(
+    AttnArgs a) {
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
