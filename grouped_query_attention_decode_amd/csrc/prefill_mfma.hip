@@ -235,6 +235,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
             }
         lsum += ps;
         // ---- O^T += V^T . P^T ----
+        // Raised wave priority for this block: while one wave of a SIMD issues its P.V
+        // products, the other wave's softmax fills the issue slots around them instead of
+        // delaying them (measured +2.5-3 % on non-causal and chunked prefill, neutral causal).
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int r0 = 16 * kk + vrow0;
@@ -250,6 +255,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
                 o[db] = mfma32x32x16(i32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kk], o[db]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     auto tile_needs_mask = [&](int k0) {
