@@ -63,6 +63,14 @@ _FAMILY_SOURCES = {
 }
 
 
+# Workloads measured in the breakdown beside those of workloads.WORKLOADS (also selectable
+# with --workload, e.g. to profile them on their own).
+EXTRA_WORKLOADS = {
+    "mqa_int4_decode_B8_L32768": W.mqa_int4_long_decode,
+    "llama70b_gqa8_decode_B16_ragged_int4": W.llama70b_ragged_decode_int4,
+    "gqa8_chunked_prefill_B4_Tq512_L4096": W.chunked_prefill_512_of_4096,
+}
+
 def kernel_sources_sha256(family: str) -> str:
     """Hash of the sources of one kernel family; counters taken on other sources do not apply."""
     import hashlib
@@ -206,7 +214,7 @@ def bench_chunk(gqa, c: W.ChunkCase, steps, warmup, dev):
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(c.name)},
     }
 
 
@@ -357,7 +365,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=HEADLINE, choices=[k for k in W.WORKLOADS if k != "toy"])
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=[k for k in W.WORKLOADS if k != "toy"] + list(EXTRA_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -388,11 +397,13 @@ def main():
     gqa.library()
 
     def run(name, steps, warmup, append=False):
-        case = W.WORKLOADS[name](0)
+        case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0)
         tag = name + ("+append" if append else "")
         log(f"[bench] {tag}: steps={steps} warmup={warmup}")
         if isinstance(case, W.PrefillCase):
             r = bench_prefill(gqa, case, steps, warmup, dev)
+        elif isinstance(case, W.ChunkCase):
+            r = bench_chunk(gqa, case, steps, warmup, dev)
         else:
             r = bench_decode(gqa, case, steps, warmup, dev, append)
         log(f"[bench] {tag}: {json.dumps(r)}")
@@ -408,22 +419,14 @@ def main():
             breakdown[name] = r
         # The decode step with the current token's cache append done by the same call.
         for name in dict.fromkeys((args.workload, "mqa_fp8_decode_B8_L32768")):
-            if W.WORKLOADS[name] is not W.causal_prefill_2048:
+            if isinstance((W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0), W.DecodeCase):
                 _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
                 breakdown[name + "+append"] = r
-        # INT4 caches (4-bit fields, one scale per sequence and KV head).
-        for wl in (W.mqa_int4_long_decode, W.llama70b_ragged_decode_int4):
-            ic = wl(0)
-            log(f"[bench] {ic.name}")
-            r = bench_decode(gqa, ic, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
-            log(f"[bench] {ic.name}: {json.dumps(r)}")
-            breakdown[ic.name] = r
-        # Prefill of a 512-token chunk against a 3584-token cache.
-        cc = W.chunked_prefill_512_of_4096(0)
-        log(f"[bench] {cc.name}")
-        r = bench_chunk(gqa, cc, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
-        log(f"[bench] {cc.name}: {json.dumps(r)}")
-        breakdown[cc.name] = r
+        # INT4 caches (4-bit fields, one scale per sequence and KV head), and prefill of a
+        # 512-token chunk against a 3584-token cache.
+        for name in EXTRA_WORKLOADS:
+            if name != args.workload:
+                _, breakdown[name] = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
         # The same decodes over a cache in shuffled pages of 16 rows.
         for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
             pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)
@@ -432,7 +435,7 @@ def main():
             log(f"[bench] {pc.name}: {json.dumps(r)}")
             breakdown[pc.name] = r
 
-    is_prefill = isinstance(case, W.PrefillCase)
+    is_prefill = isinstance(case, (W.PrefillCase, W.ChunkCase))
     cpu = None
     if not args.no_cpu_baseline and not is_prefill:
         log("[bench] cpu baseline (oracle) ...")
@@ -443,10 +446,12 @@ def main():
         value, unit, dtype = head["tflops"], "TFLOP/s", "bf16"
     else:
         value, unit = head["kv_read_GBps"], "GB/s"
-        dtype = {W.BF16: "bf16", W.FP8: "fp8_e4m3fn", W.F32: "f32"}[case.kv_dtype]
+        dtype = {W.BF16: "bf16", W.FP8: "fp8_e4m3fn", W.F32: "f32", W.INT4: "int4"}[case.kv_dtype]
     cfg = {"workload": case.name, "global_batch": case.B, "heads": case.H, "kv_heads": case.G,
            "head_dim": case.D, "parallelism": "none (1 GPU)"}
-    if is_prefill:
+    if isinstance(case, W.ChunkCase):
+        cfg["seq_len"], cfg["chunk_len"] = case.T_cap, case.Tq
+    elif is_prefill:
         cfg["seq_len"] = case.T
     else:
         cfg["kv_cache_len"] = case.T_cap
