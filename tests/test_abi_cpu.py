@@ -154,6 +154,10 @@ def test_split_queries(lib):
                  (1, 4, 2, 3, 7, "f32")]:
         s = gqa.decode_num_splits(*args)
         assert 1 <= s <= args[4] and s == gqa.decode_num_splits(*args)
+    # small INT4 rows: the ranges still give every one of the 256 CUs a workgroup (8 x 32)
+    assert gqa.decode_num_splits(8, 32, 1, 128, 32768, "int4") == 32
+    # ... but no range shorter than one 64-key tile
+    assert gqa.decode_num_splits(1, 32, 1, 128, 640, "int4") == 10
     # invalid sizes
     assert gqa.decode_num_splits(0, 8, 2, 64, 10) == 0
     assert gqa.decode_workspace_size(1, 6, 4, 64, 10) == 2 ** 64 - 1
