@@ -67,15 +67,22 @@ template <int KV> constexpr int kLdsRowBytes = KV == KV_FP8 ? 128 : 256;
 // 136 * sum(q) from each score, 136 * sum(p) from each output.
 constexpr float kI4Offset = 136.f;
 
-// Eight INT4 fields (byte i: field 2i low, 2i+1 high) -> eight bf16 values 136 + code.
+// Eight INT4 fields (byte i: field 2i low, 2i+1 high) -> eight bf16 values 136 + code, in
+// nine instructions: the fields are masked out one per byte (even and odd fields), gathered
+// into byte order by two byte permutes, and each output dword is one permute that puts the
+// bf16 high byte 0x43 above two of them. (perm(s0, s1, sel): result byte k is byte sel_k of
+// s0:s1, s1 being bytes 0-3.)
 __device__ __forceinline__ i32x4_t i4x8_to_bf16x8(int w) {
     const uint32_t x = (uint32_t)w;
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;  // fields 2i, 2i+1
+    const uint32_t f03 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // fields 0..3
+    const uint32_t f47 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // fields 4..7
+    const uint32_t c = 0x43434343u;
     i32x4_t r;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t t = (x >> (8 * m)) & 0xFFu;
-        r[m] = (int)(0x43004300u | (t & 0xFu) | ((t & 0xF0u) << 12));
-    }
+    r[0] = (int)__builtin_amdgcn_perm(c, f03, 0x04010400u);
+    r[1] = (int)__builtin_amdgcn_perm(c, f03, 0x04030402u);
+    r[2] = (int)__builtin_amdgcn_perm(c, f47, 0x04010400u);
+    r[3] = (int)__builtin_amdgcn_perm(c, f47, 0x04030402u);
     return r;
 }
 
