@@ -66,6 +66,7 @@ template <int KV> constexpr int kLdsRowBytes = KV == KV_FP8 ? 128 : 256;
 // has unit spacing in [128, 256)). The constant 136 is taken out of the products afterwards:
 // 136 * sum(q) from each score, 136 * sum(p) from each output.
 constexpr float kI4Offset = 136.f;
+constexpr float kRescaleSlack = 8.f;  // base-2 headroom of the lazy softmax reference
 
 // Eight INT4 fields (byte i: field 2i low, 2i+1 high) -> eight bf16 values 136 + code, in
 // nine instructions: the fields are masked out one per byte (even and odd fields), gathered
@@ -342,13 +343,16 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 
     // One 32-token block: `slot` holds its K/V rows (requested earlier) and is refilled with
     // the block `dist` rows ahead (dist = 0: the wave's last block, nothing to refill).
-    auto step = [&](Frag<KV> &slot, int t0, int dist) {
+    // tail: std::true_type for the wave's last block, the only one that can reach past the end
+    // of the range; only there are rows masked by index.
+    auto step = [&](Frag<KV> &slot, int t0, int dist, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
         Frag<KV> cur = slot;
         // Rows at or past the end may hold anything, NaN included (a first block requested
         // before the length was known reads up to the allocation). Their scores are masked by
         // index below; zero their values so that the zero probabilities stay exact. (Every
         // INT4 field is finite: nothing to clear.)
-        if (!I4 && t0 + kBlockT > ke) {
+        if (!I4 && TAIL && t0 + kBlockT > ke) {
             if constexpr (FP8) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -430,28 +434,44 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = tl + 4 * blk + i;
-                    const float v = t < ke ? (s[hb][blk][i] - qoff[hb]) * c : -INFINITY;
+                    const float v = !TAIL || t < ke ? (s[hb][blk][i] - qoff[hb]) * c : -INFINITY;
                     x[blk * 4 + i] = v;
                     bm = fmaxf(bm, v);
                 }
             bm = fmaxf(bm, __shfl_xor(bm, 16));
             bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float mn = fmaxf(m[hb], bm);
-            const float alpha = fast_exp2(m[hb] - mn);
+            // Running max, rescaled every block, on the wave's last block (a wave with a single
+            // block pays no test); lazily before it: the reference m moves only when a head's
+            // max outgrows it by more than kRescaleSlack, so p <= 2^kRescaleSlack and most
+            // blocks skip the O rescale (the merge only needs m, l and O to agree).
+            float alpha = 1.f;
+            bool resc = TAIL;
+            if constexpr (TAIL) {
+                const float mn = fmaxf(m[hb], bm);
+                alpha = fast_exp2(m[hb] - mn);
+                m[hb] = mn;
+            } else if (__any(bm > m[hb] + kRescaleSlack)) {
+                const float mn = fmaxf(m[hb], bm);
+                alpha = fast_exp2(m[hb] - mn);
+                m[hb] = mn;
+                resc = true;
+            }
+            const float mr = m[hb];
             float ps = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                x[e] = fast_exp2(x[e] - mn);
+                x[e] = fast_exp2(x[e] - mr);
                 ps += x[e];
             }
             lsum[hb] = lsum[hb] * alpha + ps;
-            m[hb] = mn;
+            if (resc) {
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                o[hb][nb][0] *= alpha;
-                o[hb][nb][1] *= alpha;
-                o[hb][nb][2] *= alpha;
-                o[hb][nb][3] *= alpha;
+                for (int nb = 0; nb < 8; ++nb) {
+                    o[hb][nb][0] *= alpha;
+                    o[hb][nb][1] *= alpha;
+                    o[hb][nb][2] *= alpha;
+                    o[hb][nb][3] *= alpha;
+                }
             }
             pb[hb][0] = pack_bf16_rne(x[0], x[1]);
             pb[hb][1] = pack_bf16_rne(x[2], x[3]);
@@ -492,9 +512,9 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         // The wave's last block is peeled off the loop: it is the one that may hold the row
         // of a cache append, and code for that kept out of the loop costs it no registers.
         const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
-        for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep);
+        for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep, std::false_type{});
         if (po.append && tl + kBlockT >= ke) append_row<KV, PAGED>(nxt, a, bg, src, tl, ke - 1, lane);
-        step(nxt, tl, 0);
+        step(nxt, tl, 0, std::true_type{});
     }
     if constexpr (I4) {
         // Take 136 * sum(p) out of every output: o held sum_t p_t (136 + code_t) v_scale-free.
