@@ -335,6 +335,31 @@ def bench_prefill(gqa, c, steps, warmup, dev):
     }
 
 
+def hbm_achievable(dev, nbytes=1 << 30, reps=5):
+    """What a plain streaming kernel reaches on this device (context beside the published
+    peak): a device copy that reads and writes nbytes, median of reps."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        res[f"{name}_GBps"] = moved / sorted(times)[len(times) // 2] / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    res["bytes"] = nbytes
+    res["note"] = "torch device copy of 1 GiB fp32; GB/s counts bytes read plus bytes written"
+    return res
+
+
 def cpu_baseline_decode(c: W.DecodeCase, budget_s=10.0):
     """The fp64 oracle on the host cores, on the same decode step (whole step, repeated)."""
     import oracle
@@ -436,6 +461,7 @@ def main():
             breakdown[pc.name] = r
 
     is_prefill = isinstance(case, (W.PrefillCase, W.ChunkCase))
+    achievable = None if args.no_breakdown else hbm_achievable(dev)
     cpu = None
     if not args.no_cpu_baseline and not is_prefill:
         log("[bench] cpu baseline (oracle) ...")
@@ -464,6 +490,7 @@ def main():
         "hbm_frac": (value / HBM_PEAK_GBS) if not is_prefill else None,
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "hbm_achievable": achievable,
         "detail": head,
         "breakdown": breakdown,
     }
