@@ -318,8 +318,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                     const uint32_t w = (uint32_t)qT[hb][kk][e];
                     sum += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
                 }
-            sum += __shfl_xor(sum, 16);
-            sum += __shfl_xor(sum, 32);
+            sum = sum_xor32(sum_xor16(sum));
             qoff[hb] = kI4Offset * sum;
         }
     }
@@ -438,8 +437,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                     x[blk * 4 + i] = v;
                     bm = fmaxf(bm, v);
                 }
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            bm = max_xor32(max_xor16(bm));
             // Running max, rescaled every block, on the wave's last block (a wave with a single
             // block pays no test); lazily before it: the reference m moves only when a head's
             // max outgrows it by more than kRescaleSlack, so p <= 2^kRescaleSlack and most
@@ -520,8 +518,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         // Take 136 * sum(p) out of every output: o held sum_t p_t (136 + code_t) v_scale-free.
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
-            lb[hb] += __shfl_xor(lb[hb], 16);
-            lb[hb] += __shfl_xor(lb[hb], 32);
+            lb[hb] = sum_xor32(sum_xor16(lb[hb]));
             const float corr = kI4Offset * lb[hb];
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -540,8 +537,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-        lsum[hb] += __shfl_xor(lsum[hb], 16);
-        lsum[hb] += __shfl_xor(lsum[hb], 32);
+        lsum[hb] = sum_xor32(sum_xor16(lsum[hb]));
         if (lane < 16) m_w[wave][hb * 16 + lane] = m[hb];
     }
     __syncthreads();

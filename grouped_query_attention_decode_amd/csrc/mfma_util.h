@@ -64,4 +64,26 @@ __device__ __forceinline__ int pack_bf16_rne(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32), result in every lane. One
+// v_permlane16_swap / v_permlane32_swap called with the same value in both operands leaves x
+// of the partner lane in one of its two outputs and x of the lane itself in the other, so
+// combining the two outputs is the pair reduction: a VALU operation instead of an LDS lane
+// shuffle on the softmax's dependency chain.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 }  // namespace gqa

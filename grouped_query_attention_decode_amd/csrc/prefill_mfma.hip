@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kh][e]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
+        tmax = max_xor32(tmax) * c;
         // ---- lazy rescale: move the reference only when the max outgrows it by > 2^8 ----
         if (__any(tmax > mref + kRescaleSlack)) {
             const float mn = fmaxf(mref, tmax);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     }
 
     // ---- epilogue: out[row][d] = O^T[d][row] / l ----
-    lsum += __shfl_xor(lsum, 32);
+    lsum = sum_xor32(lsum);
     if (row_ok) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         uint16_t *op = static_cast<uint16_t *>(a.out) + qrow * kD;
