@@ -86,4 +86,10 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// DPP lane move (a VALU operand modifier, no LDS round trip): quad_perm within groups of four
+// lanes (0xB1: lane ^ 1, 0x4E: lane ^ 2) and row_ror within rows of 16 (0x124: by 4, 0x128: by 8).
+template <int CTRL> __device__ __forceinline__ int dpp_move(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
 }  // namespace gqa

@@ -214,11 +214,17 @@ __device__ __forceinline__ int flat_chunk(int N, int nw, int cmin) {
     return (c + 31) & ~31;
 }
 
-// Wave-wide sum of one value per lane.
+// Wave-wide sum of one value per lane: rows of 16 by two rotations and two quad permutes,
+// then the four rows by two lane swaps.
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+    x += dpp_move<0x128>(x);
+    x += dpp_move<0x124>(x);
+    x += dpp_move<0x4E>(x);
+    x += dpp_move<0xB1>(x);
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(p[0] + p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)(q[0] + q[1]);
 }
 
 // Wave-wide inclusive prefix sum of one value per lane.
