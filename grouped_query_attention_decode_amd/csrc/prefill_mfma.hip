@@ -69,21 +69,35 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// Direct global -> LDS load of one 64-key tile of K or V (16 KB); each of the 4 waves moves
+// Direct buffer -> LDS load of one 64-key tile of K or V (16 KB); each of the 4 waves moves
 // 4 KB (four 1 KB instructions). Lane l of instruction n fills LDS slot 64n + l: tile row
-// r = 4n + l/16, position p = l%16, which holds chunk p ^ swz(r) of key row k0 + r (clamped
-// to the last row, T-1, past the end).
-__device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k0, int T, int wave, int lane) {
+// r = 4n + l/16, position p = l%16, which holds chunk p ^ swz(r) of key row k0 + r. The
+// buffer resource (built with scalar instructions) starts at row k0 and covers only the rows
+// below L, so rows past the end read as zeros: their scores are masked and their zero values
+// add nothing. The per-lane byte offsets are the same for every tile (TileOffs), so a tile
+// load costs no vector arithmetic.
+struct TileOffs {
+    int o0, o1, o2, o3;
+};
+__device__ __forceinline__ TileOffs tile_offsets(int wave, int lane) {
+    int o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int n = wave * 4 + q;
-        const int r = 4 * n + (lane >> 4);
-        int key = k0 + r;
-        key = key < T ? key : T - 1;
-        const int c = (lane & 15) ^ swz(r);
-        __builtin_amdgcn_global_load_lds((const void *)(src + (long)key * kRowBytes + 16 * c),
-                                         GQA_LDS(void, lds_tile + n * 1024), 16, 0, 0);
+        const int r = 4 * (wave * 4 + q) + (lane >> 4);
+        o[q] = r * kRowBytes + 16 * ((lane & 15) ^ swz(r));
     }
+    return TileOffs{o[0], o[1], o[2], o[3]};
+}
+__device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k0, int L, int wave, TileOffs t) {
+    const int rows = L - k0;
+    const int bytes = rows <= 0 ? 0 : (rows < kBN ? rows : kBN) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(src + (long)k0 * kRowBytes), 0, bytes, 0x00020000);
+    char *const dst = lds_tile + wave * 4 * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst), 16, t.o0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst + 1024), 16, t.o1, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst + 2048), 16, t.o2, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst + 3072), 16, t.o3, 0, 0, 0);
 }
 
 template <int R, bool CAUSAL, bool CACHED>
@@ -144,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     const int wg_last = off + (p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1);
     const int nkt = CAUSAL ? (wg_last < 0 ? 0 : wg_last / kBN + 1) : (Lb + kBN - 1) / kBN;
     const int wave_min_pos = off + (P >= 32 ? p0 + (32 * wave) % P : p0);
-    const int kmax = Lb > 0 ? Lb : 1;  // tile loads clamp to the last valid row (row 0 when none)
+    const TileOffs toffs = tile_offsets(wave, lane);
 
     f32x16_t o[4];
 #pragma unroll
@@ -153,15 +167,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
     float mref = -INFINITY, lsum = 0.f;
 
-    // Per-lane constant parts of the LDS addresses.
+    // Per-lane constant parts of the LDS addresses. K operand, key half kh: row r and chunk
+    // (2 ks + hl) ^ swz(r); since 2 ks + hl = 2 ks ^ hl, the byte offset is
+    // kofs[kh] ^ 32 ks with kofs[kh] = 256 r + 16 (hl ^ swz(r)).
     const int hl = lane >> 5;
-    int kaddr[2];
+    int kofs[2];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) kaddr[kh] = (32 * kh + tau(lane & 31));
+    for (int kh = 0; kh < 2; ++kh) {
+        const int r = 32 * kh + tau(lane & 31);
+        kofs[kh] = r * kRowBytes + 16 * (hl ^ swz(r));
+    }
+    // V operand: rows 16 kk + vrow0 (+4 for the upper half) have the swizzle of vrow0 (+4), so
+    // the offset is 4096 kk (an immediate) plus one of eight per-lane constants.
     const int gq = lane >> 4, jj = lane & 15;
-    const int vrow0 = 8 * (gq >> 1) + (jj >> 2);                    // + 16 kk (+4 for the upper half)
+    const int vrow0 = 8 * (gq >> 1) + (jj >> 2);
     const int vcol = 16 * (gq & 1) + 4 * (jj & 3);                  // + 32 db
     const int voff = (vcol & 7) * 2;
+    int vofs[2][4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int chn = (32 * db + vcol) >> 3;
+        vofs[0][db] = vrow0 * kRowBytes + voff + 16 * (chn ^ swz(vrow0));
+        vofs[1][db] = (vrow0 + 4) * kRowBytes + voff + 16 * (chn ^ swz(vrow0 + 4));
+    }
 
     auto compute_tile = [&](const char *kt, const char *vt, int k0, bool need_mask) {
         // ---- S^T = K . Q^T; the two 32-key halves accumulate independently, so
@@ -175,8 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const int r = kaddr[kh];
-                const i32x4_t ka = *(const i32x4_t *)(kt + r * kRowBytes + 16 * ((2 * ks + hl) ^ swz(r)));
+                const i32x4_t ka = *(const i32x4_t *)(kt + (kofs[kh] ^ (32 * ks)));
                 s[kh] = mfma32x32x16(ka, qT[ks], s[kh]);
             }
         // K-operand reads lead their MFMAs by two k-steps, so their LDS latency overlaps
@@ -242,16 +269,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int r0 = 16 * kk + vrow0;
-            const int r1 = r0 + 4;
-            const char *v0 = vt + r0 * kRowBytes + voff;
-            const char *v1 = vt + r1 * kRowBytes + voff;
-            const int s0 = swz(r0), s1 = swz(r1);
+            const char *vk = vt + 16 * kk * kRowBytes;
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                const int chn = (32 * db + vcol) >> 3;
-                const i32x2_t lo = lds_read_tr16(v0 + 16 * (chn ^ s0));
-                const i32x2_t hi = lds_read_tr16(v1 + 16 * (chn ^ s1));
+                const i32x2_t lo = lds_read_tr16(vk + vofs[0][db]);
+                const i32x2_t hi = lds_read_tr16(vk + vofs[1][db]);
                 o[db] = mfma32x32x16(i32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kk], o[db]);
             }
         }
@@ -263,22 +285,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > Lb);
     };
 
-    load_tile(k_lds0, kbase, 0, kmax, wave, lane);
-    load_tile(v_lds0, vbase, 0, kmax, wave, lane);
+    load_tile(k_lds0, kbase, 0, Lb, wave, toffs);
+    load_tile(v_lds0, vbase, 0, Lb, wave, toffs);
     wait_vmem_all();
     __syncthreads();
     for (int kt = 0; kt < nkt; kt += 2) {
         if (kt + 1 < nkt) {
-            load_tile(k_lds1, kbase, (kt + 1) * kBN, kmax, wave, lane);
-            load_tile(v_lds1, vbase, (kt + 1) * kBN, kmax, wave, lane);
+            load_tile(k_lds1, kbase, (kt + 1) * kBN, Lb, wave, toffs);
+            load_tile(v_lds1, vbase, (kt + 1) * kBN, Lb, wave, toffs);
         }
         compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
         wait_vmem_all();
         __syncthreads();
         if (kt + 1 >= nkt) break;
         if (kt + 2 < nkt) {
-            load_tile(k_lds0, kbase, (kt + 2) * kBN, kmax, wave, lane);
-            load_tile(v_lds0, vbase, (kt + 2) * kBN, kmax, wave, lane);
+            load_tile(k_lds0, kbase, (kt + 2) * kBN, Lb, wave, toffs);
+            load_tile(v_lds0, vbase, (kt + 2) * kBN, Lb, wave, toffs);
         }
         compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
         wait_vmem_all();
