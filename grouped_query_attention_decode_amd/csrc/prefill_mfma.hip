@@ -100,9 +100,12 @@ __device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst + 3072), 16, t.o3, 0, 0, 0);
 }
 
+// R: query heads per KV head, a power of two; 0 = any R <= 64, read at run time (the
+// workgroup then holds floor(128 / R) positions of each head and its last 128 mod R rows idle).
 template <int R, bool CAUSAL, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
-    constexpr int P = kRows / R;  // positions per workgroup
+    const int Rr = R > 0 ? R : a.H / a.G;
+    const int P = kRows / Rr;  // positions per workgroup
     __shared__ __attribute__((aligned(16))) char k_lds0[kTileBytes];
     __shared__ __attribute__((aligned(16))) char v_lds0[kTileBytes];
     __shared__ __attribute__((aligned(16))) char k_lds1[kTileBytes];
@@ -130,9 +133,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
 
     // This lane's query row.
     const int wr = 32 * wave + (lane & 31);  // row inside the workgroup
-    const int head = g * R + wr / P;
+    const int hq = wr / P;  // head of the group (Rr: an idle row, loads clamped into the group)
+    const int head = g * Rr + (hq < Rr ? hq : Rr - 1);
     const int pos = p0 + wr % P;
-    const bool row_ok = pos < T;
+    const bool row_ok = hq < Rr && pos < T;
     const long qrow = ((long)b * H + head) * T + (row_ok ? pos : T - 1);
 
     // Base-2 score scale; a negative scale is folded into Q so that c > 0 and the row max
@@ -157,7 +161,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     // Keys this workgroup needs (absolute positions), and the smallest position of this wave.
     const int wg_last = off + (p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1);
     const int nkt = CAUSAL ? (wg_last < 0 ? 0 : wg_last / kBN + 1) : (Lb + kBN - 1) / kBN;
-    const int wave_min_pos = off + (P >= 32 ? p0 + (32 * wave) % P : p0);
+    // The wave's 32 rows start at position (32 w) mod P and wrap to 0 if they cross a head.
+    const int wm0 = (32 * wave) % P;
+    const int wave_min_pos = off + p0 + (wm0 + 31 < P ? wm0 : 0);
     const TileOffs toffs = tile_offsets(wave, lane);
 
     f32x16_t o[4];
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
 
 template <int R>
 hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
-    constexpr int P = kRows / R;
+    const int P = kRows / (R > 0 ? R : a.H / a.G);
     const int npt = (a.Tq + P - 1) / P;
     dim3 grid((unsigned)(a.B * a.G * npt));
     if (a.cached) {
@@ -349,7 +355,7 @@ hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
 bool prefill_mfma_supports(const AttnArgs &a) {
     if (a.decode || a.D != kD || a.q_dtype != DT_BF16 || a.kv_dtype != DT_BF16) return false;
     const int R = a.H / a.G;
-    return R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32 || R == 64;
+    return R >= 1 && R <= 64;
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream) {
@@ -361,7 +367,8 @@ hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream) {
         case 8: return launch_r<8>(a, stream);
         case 16: return launch_r<16>(a, stream);
         case 32: return launch_r<32>(a, stream);
-        default: return launch_r<64>(a, stream);
+        case 64: return launch_r<64>(a, stream);
+        default: return launch_r<0>(a, stream);
     }
 }
 

@@ -226,7 +226,7 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
  * rows 0 .. p; causal = 0: to rows 0 .. seq_lens[b]-1. seq_lens is read as in gqa_decode (a
  * value above T_cap is T_cap, below 0 is 0); a query with p < 0 sees no row and its output is
  * zero. Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16) -- matrix cores for D = 128
- * and R a power of two up to 64 -- and (BF16, FP8_E4M3FN) with opts->k_scale / v_scale as in
+ * and R up to 64 -- and (BF16, FP8_E4M3FN) with opts->k_scale / v_scale as in
  * gqa_decode (generic family). D in 1..256.
  */
 gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,

@@ -65,6 +65,8 @@ CHUNK_CASES = [
     (1, 64, 1, 128, 33, [700], 800, W.BF16, W.BF16, True),         # MQA, R = 64
     (2, 6, 3, 80, 9, [40, 3], 41, W.F32, W.F32, True),             # fp32, odd head dim (generic)
     (2, 32, 8, 128, 33, [300, 40], 300, W.BF16, W.FP8, True),      # fp8 cache (generic)
+    (2, 28, 4, 128, 50, [600, 50], 640, W.BF16, W.BF16, True),      # R = 7
+    (1, 40, 8, 128, 33, [400], 400, W.BF16, W.BF16, False),        # R = 5, not causal
 ]
 
 

@@ -242,6 +242,10 @@ PREFILL_CASES = [
     (1, 2, 1, 128, 1, True, W.BF16),        # a single position
     (1, 6, 3, 96, 70, True, W.F32),
     (1, 4, 2, 64, 100, False, W.BF16),
+    (1, 28, 4, 128, 300, True, W.BF16),     # R = 7 (query heads per KV head not a power of two)
+    (2, 40, 8, 128, 130, False, W.BF16),    # R = 5
+    (1, 36, 3, 128, 257, True, W.BF16),     # R = 12
+    (1, 48, 1, 128, 70, True, W.BF16),      # R = 48: two positions per workgroup
 ]
 
 
@@ -249,7 +253,8 @@ PREFILL_CASES = [
 def test_prefill_cases(gqa, B, H, G, D, T, causal, dt):
     c = W.make_prefill(B, H, G, D, T, dtype=dt, causal=causal, seed=T + D, name=f"prefill_B{B}H{H}G{G}D{D}T{T}")
     want = oracle.prefill(c)
-    for path in ("auto", "generic"):
+    paths = ("auto", "generic") + (("mfma",) if D == 128 and dt == W.BF16 else ())
+    for path in paths:
         check(dev_prefill(gqa, c, path=path), want, TOL[dt], f"{c.name} causal={causal} path={path}")
 
 
