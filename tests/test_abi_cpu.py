@@ -209,7 +209,8 @@ def _chunk(lib, B=2, Tq=16, H=8, G=2, D=128, scale=0.1, causal=1, ptrs=(FAKE,) *
     (dict(kv_dtype=2), INV),                            # fp8 without scales
     (dict(path=2), UNS),                                # no vector-ALU prefill
     (dict(q_dtype=0, kv_dtype=0, path=3), UNS),         # matrix cores: bf16 only
-    (dict(H=12, G=4, path=3), UNS),                     # matrix cores: R a power of two
+    (dict(H=130, G=2, path=3), UNS),                    # matrix cores: R up to 64
+    (dict(D=64, path=3), UNS),                          # matrix cores: D = 128
     (dict(path=7), INV),
 ])
 def test_prefill_cached_rejects(lib, kw, code):
