@@ -100,9 +100,38 @@ __device__ __forceinline__ void load_tile(char *lds_tile, const char *src, int k
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQA_LDS(void, dst + 3072), 16, t.o3, 0, 0, 0);
 }
 
+// fp8 (E4M3FN) cache rows: 128 bytes. A wave fetches 16 of a tile's 64 rows into registers --
+// lane l, i = 0, 1: row 16 w + 8 i + l/8, 16-byte chunk l % 8 (dims 16 (l % 8) .. +15) --
+// through a buffer resource that covers only the rows below L (rows past it read as zeros),
+// and later widens them (exactly) into the bf16 tile layout above, so the products are the
+// same as for a bf16 cache and the conversion happens once per tile, not once per wave.
+constexpr int kRowBytesF8 = kD;
+__device__ __forceinline__ void fetch_tile_f8(i32x4_t (&f)[2], const char *src, int k0, int L, int wave, int lane) {
+    const int rows = L - k0;
+    const int bytes = rows <= 0 ? 0 : (rows < kBN ? rows : kBN) * kRowBytesF8;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(src + (long)k0 * kRowBytesF8), 0, bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * wave + 8 * i + (lane >> 3);
+        f[i] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, r * kRowBytesF8 + 16 * (lane & 7), 0, 0));
+    }
+}
+__device__ __forceinline__ void stage_tile_f8(char *lds_tile, const i32x4_t (&f)[2], int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * wave + 8 * i + (lane >> 3), c = lane & 7;
+        char *row = lds_tile + r * kRowBytes;
+        *(i32x4_t *)(row + 16 * ((2 * c) ^ swz(r))) = e4m3x8_to_bf16x8(i32x2_t{f[i][0], f[i][1]});
+        *(i32x4_t *)(row + 16 * ((2 * c + 1) ^ swz(r))) = e4m3x8_to_bf16x8(i32x2_t{f[i][2], f[i][3]});
+    }
+}
+
 // R: query heads per KV head, a power of two; 0 = any R <= 64, read at run time (the
 // workgroup then holds floor(128 / R) positions of each head and its last 128 mod R rows idle).
-template <int R, bool CAUSAL, bool CACHED>
+// F8: the cache holds E4M3FN codes with one k and one v scale per (sequence, KV head) (chunk
+// against a cache only): k_scale joins the score scale, v_scale the final division.
+template <int R, bool CAUSAL, bool CACHED, bool F8 = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     const int Rr = R > 0 ? R : a.H / a.G;
     const int P = kRows / Rr;  // positions per workgroup
@@ -142,6 +171,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     // Base-2 score scale; a negative scale is folded into Q so that c > 0 and the row max
     // can be taken on the raw scores.
     float c = a.scale_log2;
+    float vscale = 1.f;
+    if constexpr (F8) {
+        c *= a.k_scale[bg];
+        vscale = a.v_scale[bg];
+    }
     const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
     c = fmaxf(fabsf(c), 1e-30f);  // a zero scale stays (numerically) uniform, without 0 * -inf
 
@@ -155,8 +189,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) qT[ks][e] ^= qsign;
     }
 
-    const char *kbase = static_cast<const char *>(a.k) + (long)bg * Tk * kRowBytes;
-    const char *vbase = static_cast<const char *>(a.v) + (long)bg * Tk * kRowBytes;
+    constexpr int kRowBytesG = F8 ? kRowBytesF8 : kRowBytes;  // cache row bytes in memory
+    const char *kbase = static_cast<const char *>(a.k) + (long)bg * Tk * kRowBytesG;
+    const char *vbase = static_cast<const char *>(a.v) + (long)bg * Tk * kRowBytesG;
 
     // Keys this workgroup needs (absolute positions), and the smallest position of this wave.
     const int wg_last = off + (p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1);
@@ -291,6 +326,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > Lb);
     };
 
+    if constexpr (F8) {
+        // Tile t+1 is fetched into registers before tile t is multiplied, then widened into
+        // the other buffer (free: every wave passed the barrier after the tile that used it).
+        i32x4_t kf[2], vf[2];
+        fetch_tile_f8(kf, kbase, 0, Lb, wave, lane);
+        fetch_tile_f8(vf, vbase, 0, Lb, wave, lane);
+        wait_vmem_all();
+        stage_tile_f8(k_lds0, kf, wave, lane);
+        stage_tile_f8(v_lds0, vf, wave, lane);
+        __syncthreads();
+        for (int kt = 0; kt < nkt; kt += 2) {
+            if (kt + 1 < nkt) {
+                fetch_tile_f8(kf, kbase, (kt + 1) * kBN, Lb, wave, lane);
+                fetch_tile_f8(vf, vbase, (kt + 1) * kBN, Lb, wave, lane);
+            }
+            compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
+            if (kt + 1 >= nkt) break;
+            wait_vmem_all();
+            stage_tile_f8(k_lds1, kf, wave, lane);
+            stage_tile_f8(v_lds1, vf, wave, lane);
+            __syncthreads();
+            if (kt + 2 < nkt) {
+                fetch_tile_f8(kf, kbase, (kt + 2) * kBN, Lb, wave, lane);
+                fetch_tile_f8(vf, vbase, (kt + 2) * kBN, Lb, wave, lane);
+            }
+            compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
+            if (kt + 2 >= nkt) break;
+            wait_vmem_all();
+            stage_tile_f8(k_lds0, kf, wave, lane);
+            stage_tile_f8(v_lds0, vf, wave, lane);
+            __syncthreads();
+        }
+    } else {
     load_tile(k_lds0, kbase, 0, Lb, wave, toffs);
     load_tile(v_lds0, vbase, 0, Lb, wave, toffs);
     wait_vmem_all();
@@ -312,11 +380,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         wait_vmem_all();
         __syncthreads();
     }
+    }
 
     // ---- epilogue: out[row][d] = O^T[d][row] / l ----
     lsum = sum_xor32(lsum);
     if (row_ok) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const float inv = lsum > 0.f ? vscale / lsum : 0.f;
         uint16_t *op = static_cast<uint16_t *>(a.out) + qrow * kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -336,7 +405,12 @@ hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
     const int P = kRows / (R > 0 ? R : a.H / a.G);
     const int npt = (a.Tq + P - 1) / P;
     dim3 grid((unsigned)(a.B * a.G * npt));
-    if (a.cached) {
+    if (a.cached && a.kv_dtype == DT_FP8) {
+        if (a.causal)
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, true, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, true, true>), grid, dim3(kThreads), 0, stream, a);
+    } else if (a.cached) {
         if (a.causal)
             hipLaunchKernelGGL((prefill_mfma_kernel<R, true, true>), grid, dim3(kThreads), 0, stream, a);
         else
@@ -353,7 +427,8 @@ hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool prefill_mfma_supports(const AttnArgs &a) {
-    if (a.decode || a.D != kD || a.q_dtype != DT_BF16 || a.kv_dtype != DT_BF16) return false;
+    if (a.decode || a.D != kD || a.q_dtype != DT_BF16) return false;
+    if (a.kv_dtype != DT_BF16 && !(a.cached && a.kv_dtype == DT_FP8)) return false;
     const int R = a.H / a.G;
     return R >= 1 && R <= 64;
 }

@@ -225,9 +225,9 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
  * Query i of sequence b sits at position p = seq_lens[b] - Tq + i. causal = 1: it attends to
  * rows 0 .. p; causal = 0: to rows 0 .. seq_lens[b]-1. seq_lens is read as in gqa_decode (a
  * value above T_cap is T_cap, below 0 is 0); a query with p < 0 sees no row and its output is
- * zero. Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16) -- matrix cores for D = 128
- * and R up to 64 -- and (BF16, FP8_E4M3FN) with opts->k_scale / v_scale as in
- * gqa_decode (generic family). D in 1..256.
+ * zero. Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16) and (BF16, FP8_E4M3FN) with
+ * opts->k_scale / v_scale as in gqa_decode; the bf16 and fp8 caches run on the matrix cores
+ * for D = 128 and R up to 64, everything else on the generic family. D in 1..256.
  */
 gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
                               void *out, int B, int Tq, int H, int G, int D, float scale, int causal,

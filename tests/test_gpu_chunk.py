@@ -3,8 +3,9 @@
 Cache rows at or beyond each sequence's length are NaN, so a kernel that reads past the
 length fails. Covered: causal and not, the matrix-core and generic families, chunks longer
 than the cache holds (leading zero rows), a chunk that is the whole sequence (= plain
-prefill), MHA and MQA groupings, fp32 and fp8 caches (generic), the 12-dim toy's last two
-tokens, and a prefill split into chunks that reproduces the one-shot prefill.
+prefill), MHA and MQA groupings, fp32 caches (generic) and fp8 caches (matrix cores and
+generic), the 12-dim toy's last two tokens, and a prefill split into chunks that reproduces
+the one-shot prefill.
 """
 
 import sys
@@ -64,7 +65,10 @@ CHUNK_CASES = [
     (2, 8, 8, 128, 70, [500, 70], 512, W.BF16, W.BF16, True),      # MHA
     (1, 64, 1, 128, 33, [700], 800, W.BF16, W.BF16, True),         # MQA, R = 64
     (2, 6, 3, 80, 9, [40, 3], 41, W.F32, W.F32, True),             # fp32, odd head dim (generic)
-    (2, 32, 8, 128, 33, [300, 40], 300, W.BF16, W.FP8, True),      # fp8 cache (generic)
+    (2, 32, 8, 128, 33, [300, 40], 300, W.BF16, W.FP8, True),      # fp8 cache
+    (2, 32, 8, 128, 100, [1000, 64], 1024, W.BF16, W.FP8, False),  # fp8, not causal
+    (3, 8, 8, 128, 70, [500, 70, 0], 512, W.BF16, W.FP8, True),    # fp8 MHA, an empty sequence
+    (1, 28, 4, 128, 129, [777], 800, W.BF16, W.FP8, True),         # fp8, R = 7
     (2, 28, 4, 128, 50, [600, 50], 640, W.BF16, W.BF16, True),      # R = 7
     (1, 40, 8, 128, 33, [400], 400, W.BF16, W.BF16, False),        # R = 5, not causal
 ]
