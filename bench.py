@@ -69,6 +69,7 @@ EXTRA_WORKLOADS = {
     "mqa_int4_decode_B8_L32768": W.mqa_int4_long_decode,
     "llama70b_gqa8_decode_B16_ragged_int4": W.llama70b_ragged_decode_int4,
     "gqa8_chunked_prefill_B4_Tq512_L4096": W.chunked_prefill_512_of_4096,
+    "gqa8_chunked_prefill_B4_Tq512_L4096_fp8": W.chunked_prefill_512_of_4096_fp8,
 }
 
 def kernel_sources_sha256(family: str) -> str:
@@ -193,24 +194,26 @@ def bench_chunk(gqa, c: W.ChunkCase, steps, warmup, dev):
     base = [c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)]
     reps = [base] + [[t.clone() for t in base] for _ in range(nrep - 1)]
     lens = c.seq_lens.to(dev)
+    ks = c.k_scale.to(dev) if c.k_scale is not None else None
+    vs = c.v_scale.to(dev) if c.v_scale is not None else None
     out = torch.empty_like(base[0])
     state = {"i": 0}
 
     def step():
         q, k, v = reps[state["i"] % nrep]
         state["i"] += 1
-        gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal)
+        gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal, k_scale=ks, v_scale=vs)
 
     t = time_steps(step, steps, warmup)
     fl = chunk_flops(c)
     s = t["ms_per_step"] * 1e-3
     achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
-    esz = 2
+    kv_esz = 1 if c.kv_dtype == W.FP8 else 2
     lsum = int(c.seq_lens.clamp(0, c.T_cap).sum())
     return {
         "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "Tq": c.Tq, "T_cap": c.T_cap,
-        "seq_lens": c.seq_lens.tolist(), "causal": c.causal, "flops": fl,
-        "algorithmic_bytes": esz * (2 * c.q.numel() + 2 * lsum * c.G * c.D), "tflops": fl / s / 1e12,
+        "seq_lens": c.seq_lens.tolist(), "causal": c.causal, "kv_dtype": c.kv_dtype, "flops": fl,
+        "algorithmic_bytes": 2 * (2 * c.q.numel()) + kv_esz * 2 * lsum * c.G * c.D, "tflops": fl / s / 1e12,
         "ms_per_step": t["ms_per_step"], "launch_us_mean": t["launch_ms_mean"] * 1e3,
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

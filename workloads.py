@@ -414,6 +414,12 @@ def chunked_prefill_512_of_4096(seed=0) -> ChunkCase:
     return make_chunk(4, 32, 8, 128, 512, 4096, T_cap=4096, seed=seed, name="gqa8_chunked_prefill_B4_Tq512_L4096")
 
 
+def chunked_prefill_512_of_4096_fp8(seed=0) -> ChunkCase:
+    """The chunked prefill against an fp8-E4M3FN cache (per-(sequence, KV head) scales)."""
+    return make_chunk(4, 32, 8, 128, 512, 4096, T_cap=4096, seed=seed, name="gqa8_chunked_prefill_B4_Tq512_L4096_fp8",
+                      kv_dtype=FP8)
+
+
 WORKLOADS = {
     "toy": None,  # prefill + two decode steps; see toy_prefill / toy_decode_steps
     "llama7b_gqa8_decode_L2048": llama7b_gqa8_decode,
