@@ -188,12 +188,16 @@ def chunk_flops(c: W.ChunkCase) -> int:
     return 4 * c.H * c.D * pairs
 
 
-def bench_chunk(gqa, c: W.ChunkCase, steps, warmup, dev):
-    kv_alloc = 2 * c.k_cache.numel() * c.k_cache.element_size()
+def bench_chunk(gqa, c, steps, warmup, dev):
+    """A ChunkCase (contiguous cache) or a PagedChunkCase (its cache in pages)."""
+    paged = isinstance(c, W.PagedChunkCase)
+    kc, vc = (c.k_pages, c.v_pages) if paged else (c.k_cache, c.v_cache)
+    kv_alloc = 2 * kc.numel() * kc.element_size()
     nrep = max(1, math.ceil(COLD_BYTES / kv_alloc))
-    base = [c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)]
+    base = [c.q.to(dev), kc.to(dev), vc.to(dev)]
     reps = [base] + [[t.clone() for t in base] for _ in range(nrep - 1)]
     lens = c.seq_lens.to(dev)
+    table = c.block_table.to(dev) if paged else None
     ks = c.k_scale.to(dev) if c.k_scale is not None else None
     vs = c.v_scale.to(dev) if c.v_scale is not None else None
     out = torch.empty_like(base[0])
@@ -202,7 +206,10 @@ def bench_chunk(gqa, c: W.ChunkCase, steps, warmup, dev):
     def step():
         q, k, v = reps[state["i"] % nrep]
         state["i"] += 1
-        gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal, k_scale=ks, v_scale=vs)
+        if paged:
+            gqa.prefill_paged(q, k, v, table, lens, out=out, scale=c.scale, causal=c.causal, k_scale=ks, v_scale=vs)
+        else:
+            gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal, k_scale=ks, v_scale=vs)
 
     t = time_steps(step, steps, warmup)
     fl = chunk_flops(c)
@@ -424,6 +431,12 @@ def main():
     import grouped_query_attention_decode_amd as gqa
     gqa.library()
 
+    def run_case(case, steps, warmup):
+        log(f"[bench] {case.name}: steps={steps} warmup={warmup}")
+        r = bench_chunk(gqa, case, steps, warmup, dev)
+        log(f"[bench] {case.name}: {json.dumps(r)}")
+        return case, r
+
     def run(name, steps, warmup, append=False):
         case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0)
         tag = name + ("+append" if append else "")
@@ -455,6 +468,9 @@ def main():
         for name in EXTRA_WORKLOADS:
             if name != args.workload:
                 _, breakdown[name] = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
+        # The chunked prefill against the same cache in shuffled pages of 16 rows.
+        pcc = W.make_paged_chunk(W.chunked_prefill_512_of_4096(0), 16, seed=1)
+        _, breakdown[pcc.name] = run_case(pcc, max(20, args.steps // 4), max(5, args.warmup // 2))
         # The same decodes over a cache in shuffled pages of 16 rows.
         for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
             pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)

@@ -21,7 +21,7 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
-__all__ = ["decode", "decode_paged", "prefill", "prefill_cached", "decode_num_splits", "decode_workspace_size", "status_string",
+__all__ = ["decode", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
@@ -93,6 +93,9 @@ def library() -> ctypes.CDLL:
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_prefill_cached.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_prefill_cached.restype = i
+    lib.gqa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp,
+                                      ctypes.POINTER(GqaOpts)]
+    lib.gqa_prefill_paged.restype = i
     lib.gqa_prefill.restype = i
     lib.gqa_decode_num_splits.argtypes = [i] * 7
     lib.gqa_decode_num_splits.restype = i
@@ -283,6 +286,20 @@ def prefill(q, k, v, out=None, scale=None, causal=True, path="auto", stream=None
     return out
 
 
+def _chunk_opts(q, cache, B, G, T_cap, k_scale, v_scale, path):
+    kv_code = _dtype_code(cache, "cache")
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap, path=PATHS[path])
+    if kv_code == DTYPES["fp8_e4m3fn"]:
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 caches need k_scale and v_scale")
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need_cuda(t, n)
+            if t.dtype != torch.float32 or t.numel() != B * G:
+                raise ValueError(f"{n} must be float32 [B*G]")
+        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    return o
+
+
 def prefill_cached(q, k_cache, v_cache, seq_lens, out=None, scale=None, causal=True, k_scale=None, v_scale=None,
                    path="auto", stream=None):
     """Prefill of a chunk of Tq positions against a cache. Returns ``out`` [B, H, Tq, D].
@@ -304,19 +321,44 @@ def prefill_cached(q, k_cache, v_cache, seq_lens, out=None, scale=None, causal=T
     _need_cuda(out, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    kv_code = _dtype_code(k_cache, "k_cache")
-    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap, path=PATHS[path])
-    if kv_code == DTYPES["fp8_e4m3fn"]:
-        if k_scale is None or v_scale is None:
-            raise ValueError("fp8 caches need k_scale and v_scale")
-        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
-            _need_cuda(t, n)
-            if t.dtype != torch.float32 or t.numel() != B * G:
-                raise ValueError(f"{n} must be float32 [B*G]")
-        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    o = _chunk_opts(q, k_cache, B, G, T_cap, k_scale, v_scale, path)
     st = library().gqa_prefill_cached(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                                       out.data_ptr(), B, Tq, H, G, D, float(scale), int(bool(causal)),
                                       _stream_handle(stream, q.device), ctypes.byref(o))
     if st != GQA_OK:
         raise GqaError(st, "gqa_prefill_cached")
+    return out
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=None, causal=True, k_scale=None,
+                  v_scale=None, path="auto", stream=None):
+    """Prefill of a chunk of Tq positions against a paged cache. Returns ``out`` [B, H, Tq, D].
+
+    ``k_pages``/``v_pages`` [num_pages, G, page_size, D] and ``block_table`` int32 [B, pages_per_seq]
+    as for ``decode_paged``; the other arguments are those of ``prefill_cached``."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens")):
+        _need_cuda(t, n)
+    if q.dim() != 4 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B,H,Tq,D], pools [num_pages,G,page_size,D] and block_table [B,pages_per_seq]")
+    B, H, Tq, D = q.shape
+    num_pages, G, page_size, Dk = k_pages.shape
+    Bt, pages_per_seq = block_table.shape
+    if Bt != B or Dk != D or block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 \
+            or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, pools, block_table (int32) and seq_lens (int32 [B])")
+    if k_pages.dtype != v_pages.dtype:
+        raise TypeError("k_pages and v_pages must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = _chunk_opts(q, k_pages, B, G, pages_per_seq * page_size, k_scale, v_scale, path)
+    st = library().gqa_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                     seq_lens.data_ptr(), out.data_ptr(), B, Tq, H, G, D, float(scale),
+                                     int(bool(causal)), page_size, pages_per_seq, num_pages,
+                                     _stream_handle(stream, q.device), ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_prefill_paged")
     return out

@@ -189,6 +189,7 @@ gqa_status check_device() {
 }
 
 }  // namespace
+
 }  // namespace gqa
 
 using namespace gqa;
@@ -368,6 +369,66 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
 }
 
 }  // namespace
+// Chunk against a cache, contiguous (pg null) or paged.
+gqa_status prefill_cached_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                               void *out, int B, int Tq, int H, int G, int D, float scale, int causal,
+                               hipStream_t stream, const gqa_opts *opts_in, const PagedDesc *pg) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
+    gqa_opts o;
+    if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
+    int ps_log2 = 0;
+    if (pg) {
+        // As for the paged decode; the capacity replaces opts->kv_capacity.
+        if (!pg->block_table || pg->pages_per_seq < 1 || pg->num_pages < 1) return GQA_ERR_INVALID_ARG;
+        if (pg->page_size < 16 || pg->page_size > (1 << 20) || (pg->page_size & (pg->page_size - 1)) != 0)
+            return GQA_ERR_INVALID_ARG;
+        while ((1 << ps_log2) < pg->page_size) ++ps_log2;
+        if ((long)pg->pages_per_seq * pg->page_size > 0x7fffffffL) return GQA_ERR_INVALID_ARG;
+        o.kv_capacity = pg->pages_per_seq * pg->page_size;
+    }
+    if (o.layout < GQA_LAYOUT_AUTO || o.layout > GQA_LAYOUT_FLAT) return GQA_ERR_INVALID_ARG;
+    if (Tq < 1 || !decode_sizes_ok(B, H, G, D, o.kv_capacity)) return GQA_ERR_INVALID_ARG;
+    if ((double)B * H * (double)Tq * D > 9.0e15 || (double)B * G * H * (double)Tq > 2.0e9) return GQA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
+    if (o.path < GQA_PATH_AUTO || o.path > GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
+    const bool pair_ok = (o.q_dtype == DT_F32 && o.kv_dtype == DT_F32) ||
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_BF16) ||
+                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8);
+    if (!pair_ok) return GQA_ERR_UNSUPPORTED;
+    if (o.kv_dtype == DT_FP8 && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.seq_lens = seq_lens;
+    a.k_scale = o.kv_dtype == DT_FP8 ? o.k_scale : nullptr;
+    a.v_scale = o.kv_dtype == DT_FP8 ? o.v_scale : nullptr;
+    a.B = B; a.H = H; a.G = G; a.D = D;
+    a.Tq = Tq; a.Tk = o.kv_capacity;
+    a.causal = causal; a.decode = 0; a.cached = 1;
+    a.num_splits = 1; a.split_len = o.kv_capacity;
+    a.scale_log2 = scale * kLog2e;
+    a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
+    if (pg) {
+        a.block_table = pg->block_table;
+        a.ps_log2 = ps_log2;
+        a.pages_per_seq = pg->pages_per_seq;
+        a.num_pages = pg->num_pages;
+    }
+
+    int path = o.path;
+    if (path == GQA_PATH_AUTO) path = prefill_mfma_supports(a) ? GQA_PATH_MFMA : GQA_PATH_GENERIC;
+    if (path == GQA_PATH_VALU) return GQA_ERR_UNSUPPORTED;
+    if (pg && path != GQA_PATH_MFMA) return GQA_ERR_UNSUPPORTED;  // paged: matrix-core family only
+    if (path == GQA_PATH_MFMA && !prefill_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
+
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+    const hipError_t e = path == GQA_PATH_MFMA ? launch_prefill_mfma(a, stream) : launch_generic(a, stream);
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 }  // namespace gqa
 
 extern "C" {
@@ -425,43 +486,17 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *out, i
 gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
                               void *out, int B, int Tq, int H, int G, int D, float scale, int causal,
                               hipStream_t stream, const gqa_opts *opts_in) {
-    if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
-    gqa_opts o;
-    if (!read_opts(opts_in, &o)) return GQA_ERR_INVALID_ARG;
-    if (o.layout < GQA_LAYOUT_AUTO || o.layout > GQA_LAYOUT_FLAT) return GQA_ERR_INVALID_ARG;
-    if (Tq < 1 || !decode_sizes_ok(B, H, G, D, o.kv_capacity)) return GQA_ERR_INVALID_ARG;
-    if ((double)B * H * (double)Tq * D > 9.0e15 || (double)B * G * H * (double)Tq > 2.0e9) return GQA_ERR_INVALID_ARG;
-    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
-    if (!isfinite(scale)) return GQA_ERR_INVALID_ARG;
-    if (o.path < GQA_PATH_AUTO || o.path > GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
-    if (!valid_dtype(o.q_dtype) || !valid_dtype(o.kv_dtype)) return GQA_ERR_INVALID_ARG;
-    const bool pair_ok = (o.q_dtype == DT_F32 && o.kv_dtype == DT_F32) ||
-                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_BF16) ||
-                         (o.q_dtype == DT_BF16 && o.kv_dtype == DT_FP8);
-    if (!pair_ok) return GQA_ERR_UNSUPPORTED;
-    if (o.kv_dtype == DT_FP8 && (!o.k_scale || !o.v_scale)) return GQA_ERR_INVALID_ARG;
+    return gqa::prefill_cached_impl(q, k_cache, v_cache, seq_lens, out, B, Tq, H, G, D, scale, causal, stream,
+                                    opts_in, nullptr);
+}
 
-    AttnArgs a;
-    memset(&a, 0, sizeof(a));
-    a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.seq_lens = seq_lens;
-    a.k_scale = o.kv_dtype == DT_FP8 ? o.k_scale : nullptr;
-    a.v_scale = o.kv_dtype == DT_FP8 ? o.v_scale : nullptr;
-    a.B = B; a.H = H; a.G = G; a.D = D;
-    a.Tq = Tq; a.Tk = o.kv_capacity;
-    a.causal = causal; a.decode = 0; a.cached = 1;
-    a.num_splits = 1; a.split_len = o.kv_capacity;
-    a.scale_log2 = scale * kLog2e;
-    a.q_dtype = o.q_dtype; a.kv_dtype = o.kv_dtype;
-
-    int path = o.path;
-    if (path == GQA_PATH_AUTO) path = prefill_mfma_supports(a) ? GQA_PATH_MFMA : GQA_PATH_GENERIC;
-    if (path == GQA_PATH_VALU) return GQA_ERR_UNSUPPORTED;
-    if (path == GQA_PATH_MFMA && !prefill_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
-
-    gqa_status st = check_device();
-    if (st != GQA_OK) return st;
-    const hipError_t e = path == GQA_PATH_MFMA ? launch_prefill_mfma(a, stream) : launch_generic(a, stream);
-    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+gqa_status gqa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, void *out, int B, int Tq, int H, int G, int D, float scale,
+                             int causal, int page_size, int pages_per_seq, int num_pages, hipStream_t stream,
+                             const gqa_opts *opts) {
+    const gqa::PagedDesc pg = {block_table, page_size, pages_per_seq, num_pages};
+    return gqa::prefill_cached_impl(q, k_pages, v_pages, seq_lens, out, B, Tq, H, G, D, scale, causal, stream, opts,
+                                    &pg);
 }
 
 }  // extern "C"

@@ -117,6 +117,53 @@ __device__ __forceinline__ void fetch_tile_f8(i32x4_t (&f)[2], const char *src, 
         f[i] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, r * kRowBytesF8 + 16 * (lane & 7), 0, 0));
     }
 }
+// Paged cache (pools [num_pages, G, page_size, D], one block-table row per sequence, read
+// through the scalar cache): the 4 (bf16) or 8 (fp8) rows one load instruction moves start at
+// a multiple of 4 or 8 and pages hold >= 16 rows, so they lie in one page and one buffer
+// resource covers them. Table entries and page ids are clamped into range (memory-safe).
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+struct PageGeo {
+    const char *k, *v;  // pools advanced to KV head g
+    long page_bytes;    // one page of all G heads
+    cint32_t *bt;       // block-table row of the sequence
+    int ps_log2, n_bt, num_pages;
+};
+template <int RB, int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const PageGeo &pg, const char *pool, int row0, int L) {
+    int pi = row0 >> pg.ps_log2;
+    pi = pi < 0 ? 0 : (pi >= pg.n_bt ? pg.n_bt - 1 : pi);
+    int page = __builtin_amdgcn_readfirstlane(pg.bt[pi]);
+    page = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
+    const int rows = L - row0;
+    const int bytes = rows <= 0 ? 0 : (rows < ROWS ? rows : ROWS) * RB;
+    const char *base = pool + page * pg.page_bytes + (long)(row0 & ((1 << pg.ps_log2) - 1)) * RB;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void load_tile_paged(char *lds_tile, const PageGeo &pg, const char *pool, int k0, int L,
+                                                int wave, TileOffs t) {
+    char *const dst = lds_tile + wave * 4 * 1024;
+    const int r0 = k0 + 16 * wave;  // first key row of this wave's four instructions
+    // Tile offsets relative to each instruction's first row (4 n rows into the tile).
+    const int n0 = wave * 4 * 4 * kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0, L), GQA_LDS(void, dst), 16,
+                                             t.o0 - n0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 4, L), GQA_LDS(void, dst + 1024),
+                                             16, t.o1 - n0 - 4 * kRowBytes, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 8, L), GQA_LDS(void, dst + 2048),
+                                             16, t.o2 - n0 - 8 * kRowBytes, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 12, L), GQA_LDS(void, dst + 3072),
+                                             16, t.o3 - n0 - 12 * kRowBytes, 0, 0, 0);
+}
+__device__ __forceinline__ void fetch_tile_f8_paged(i32x4_t (&f)[2], const PageGeo &pg, const char *pool, int k0, int L,
+                                                    int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc<kRowBytesF8, 8>(pg, pool, k0 + 16 * wave + 8 * i, L);
+        f[i] = __builtin_bit_cast(i32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rs, (lane >> 3) * kRowBytesF8 + 16 * (lane & 7), 0, 0));
+    }
+}
+
 __device__ __forceinline__ void stage_tile_f8(char *lds_tile, const i32x4_t (&f)[2], int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -131,7 +178,8 @@ __device__ __forceinline__ void stage_tile_f8(char *lds_tile, const i32x4_t (&f)
 // workgroup then holds floor(128 / R) positions of each head and its last 128 mod R rows idle).
 // F8: the cache holds E4M3FN codes with one k and one v scale per (sequence, KV head) (chunk
 // against a cache only): k_scale joins the score scale, v_scale the final division.
-template <int R, bool CAUSAL, bool CACHED, bool F8 = false>
+// PG: the cache lives in pages (chunk against a cache only).
+template <int R, bool CAUSAL, bool CACHED, bool F8 = false, bool PG = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     const int Rr = R > 0 ? R : a.H / a.G;
     const int P = kRows / Rr;  // positions per workgroup
@@ -192,6 +240,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     constexpr int kRowBytesG = F8 ? kRowBytesF8 : kRowBytes;  // cache row bytes in memory
     const char *kbase = static_cast<const char *>(a.k) + (long)bg * Tk * kRowBytesG;
     const char *vbase = static_cast<const char *>(a.v) + (long)bg * Tk * kRowBytesG;
+    PageGeo pgeo = {};
+    if constexpr (PG) {
+        const long ps_bytes = (long)kRowBytesG << a.ps_log2;
+        pgeo.k = static_cast<const char *>(a.k) + g * ps_bytes;
+        pgeo.v = static_cast<const char *>(a.v) + g * ps_bytes;
+        pgeo.page_bytes = G * ps_bytes;
+        pgeo.bt = (cint32_t *)(a.block_table + (long)b * a.pages_per_seq);
+        pgeo.ps_log2 = a.ps_log2;
+        pgeo.n_bt = a.pages_per_seq;
+        pgeo.num_pages = a.num_pages;
+    }
+    // Fetch / load the K and V tile starting at key k0 (contiguous or paged).
+    auto fetch_f8 = [&](i32x4_t (&kf)[2], i32x4_t (&vf)[2], int k0) __attribute__((always_inline)) {
+        if constexpr (PG) {
+            fetch_tile_f8_paged(kf, pgeo, pgeo.k, k0, Lb, wave, lane);
+            fetch_tile_f8_paged(vf, pgeo, pgeo.v, k0, Lb, wave, lane);
+        } else {
+            fetch_tile_f8(kf, kbase, k0, Lb, wave, lane);
+            fetch_tile_f8(vf, vbase, k0, Lb, wave, lane);
+        }
+    };
 
     // Keys this workgroup needs (absolute positions), and the smallest position of this wave.
     const int wg_last = off + (p0 + P - 1 < T - 1 ? p0 + P - 1 : T - 1);
@@ -322,6 +391,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_s_setprio(0);
     };
 
+    auto load_kv = [&](char *kl, char *vl, int k0) __attribute__((always_inline)) {
+        if constexpr (PG) {
+            load_tile_paged(kl, pgeo, pgeo.k, k0, Lb, wave, toffs);
+            load_tile_paged(vl, pgeo, pgeo.v, k0, Lb, wave, toffs);
+        } else {
+            load_tile(kl, kbase, k0, Lb, wave, toffs);
+            load_tile(vl, vbase, k0, Lb, wave, toffs);
+        }
+    };
+
     auto tile_needs_mask = [&](int k0) {
         return (CAUSAL && k0 + kBN - 1 > wave_min_pos) || (k0 + kBN > Lb);
     };
@@ -330,16 +409,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
         // Tile t+1 is fetched into registers before tile t is multiplied, then widened into
         // the other buffer (free: every wave passed the barrier after the tile that used it).
         i32x4_t kf[2], vf[2];
-        fetch_tile_f8(kf, kbase, 0, Lb, wave, lane);
-        fetch_tile_f8(vf, vbase, 0, Lb, wave, lane);
+        fetch_f8(kf, vf, 0);
         wait_vmem_all();
         stage_tile_f8(k_lds0, kf, wave, lane);
         stage_tile_f8(v_lds0, vf, wave, lane);
         __syncthreads();
         for (int kt = 0; kt < nkt; kt += 2) {
             if (kt + 1 < nkt) {
-                fetch_tile_f8(kf, kbase, (kt + 1) * kBN, Lb, wave, lane);
-                fetch_tile_f8(vf, vbase, (kt + 1) * kBN, Lb, wave, lane);
+                fetch_f8(kf, vf, (kt + 1) * kBN);
             }
             compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
             if (kt + 1 >= nkt) break;
@@ -348,8 +425,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
             stage_tile_f8(v_lds1, vf, wave, lane);
             __syncthreads();
             if (kt + 2 < nkt) {
-                fetch_tile_f8(kf, kbase, (kt + 2) * kBN, Lb, wave, lane);
-                fetch_tile_f8(vf, vbase, (kt + 2) * kBN, Lb, wave, lane);
+                fetch_f8(kf, vf, (kt + 2) * kBN);
             }
             compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
             if (kt + 2 >= nkt) break;
@@ -359,22 +435,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
             __syncthreads();
         }
     } else {
-    load_tile(k_lds0, kbase, 0, Lb, wave, toffs);
-    load_tile(v_lds0, vbase, 0, Lb, wave, toffs);
+    load_kv(k_lds0, v_lds0, 0);
     wait_vmem_all();
     __syncthreads();
     for (int kt = 0; kt < nkt; kt += 2) {
         if (kt + 1 < nkt) {
-            load_tile(k_lds1, kbase, (kt + 1) * kBN, Lb, wave, toffs);
-            load_tile(v_lds1, vbase, (kt + 1) * kBN, Lb, wave, toffs);
+            load_kv(k_lds1, v_lds1, (kt + 1) * kBN);
         }
         compute_tile(k_lds0, v_lds0, kt * kBN, tile_needs_mask(kt * kBN));
         wait_vmem_all();
         __syncthreads();
         if (kt + 1 >= nkt) break;
         if (kt + 2 < nkt) {
-            load_tile(k_lds0, kbase, (kt + 2) * kBN, Lb, wave, toffs);
-            load_tile(v_lds0, vbase, (kt + 2) * kBN, Lb, wave, toffs);
+            load_kv(k_lds0, v_lds0, (kt + 2) * kBN);
         }
         compute_tile(k_lds1, v_lds1, (kt + 1) * kBN, tile_needs_mask((kt + 1) * kBN));
         wait_vmem_all();
@@ -405,22 +478,29 @@ hipError_t launch_r(const AttnArgs &a, hipStream_t stream) {
     const int P = kRows / (R > 0 ? R : a.H / a.G);
     const int npt = (a.Tq + P - 1) / P;
     dim3 grid((unsigned)(a.B * a.G * npt));
-    if (a.cached && a.kv_dtype == DT_FP8) {
-        if (a.causal)
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, true, true>), grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, true, true>), grid, dim3(kThreads), 0, stream, a);
+#define GQA_PREFILL(C, K, F, PG) hipLaunchKernelGGL((prefill_mfma_kernel<R, C, K, F, PG>), grid, dim3(kThreads), 0, stream, a)
+    const bool f8 = a.kv_dtype == DT_FP8, pg = a.block_table != nullptr;
+    if (a.cached && pg) {
+        if (f8) {
+            if (a.causal) GQA_PREFILL(true, true, true, true);
+            else GQA_PREFILL(false, true, true, true);
+        } else {
+            if (a.causal) GQA_PREFILL(true, true, false, true);
+            else GQA_PREFILL(false, true, false, true);
+        }
     } else if (a.cached) {
-        if (a.causal)
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, true>), grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, true>), grid, dim3(kThreads), 0, stream, a);
+        if (f8) {
+            if (a.causal) GQA_PREFILL(true, true, true, false);
+            else GQA_PREFILL(false, true, true, false);
+        } else {
+            if (a.causal) GQA_PREFILL(true, true, false, false);
+            else GQA_PREFILL(false, true, false, false);
+        }
     } else {
-        if (a.causal)
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, true, false>), grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_mfma_kernel<R, false, false>), grid, dim3(kThreads), 0, stream, a);
+        if (a.causal) GQA_PREFILL(true, false, false, false);
+        else GQA_PREFILL(false, false, false, false);
     }
+#undef GQA_PREFILL
     return hipGetLastError();
 }
 

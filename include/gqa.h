@@ -233,6 +233,22 @@ gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_
                               void *out, int B, int Tq, int H, int G, int D, float scale, int causal,
                               hipStream_t stream, const gqa_opts *opts);
 
+/*
+ * Chunk against a paged cache: gqa_prefill_cached with the cache rows in pages, laid out as
+ * for gqa_decode_paged (pools [num_pages, G, page_size, D], int32 block_table
+ * [B, pages_per_seq] in device memory; row t of (b, g) is row t mod page_size of page
+ * block_table[b][t / page_size]; capacity pages_per_seq * page_size replaces
+ * opts->kv_capacity). The chunk's rows are written into their pages by the caller first.
+ * page_size: a power of two from 16 to 2^20. Only table entries covering rows below
+ * seq_lens[b] are read; entries outside [0, num_pages) are clamped (memory-safe, result
+ * unspecified). Kernel family: matrix cores only (bf16 q with a bf16 or fp8 cache,
+ * D = 128, R up to 64); anything else returns GQA_ERR_UNSUPPORTED.
+ */
+gqa_status gqa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, void *out, int B, int Tq, int H, int G, int D, float scale,
+                             int causal, int page_size, int pages_per_seq, int num_pages, hipStream_t stream,
+                             const gqa_opts *opts);
+
 /* Key ranges per (sequence, KV head) -- with the flat layout, the most partial results one
  * query head can have -- that gqa_decode uses for these sizes with path and layout AUTO
  * (num_splits 0 = the library's own choice, which depends only on these arguments). Returns 0

@@ -294,6 +294,15 @@ class Oracle:
             k, v = case.k_cache, case.v_cache
         return self.prefill_cached_arrays(case.q, k, v, case.seq_lens.numpy(), case.scale, case.causal)
 
+    def prefill_paged(self, case) -> np.ndarray:
+        """Oracle output [B, H, Tq, D] for a paged chunk case: prefill_cached over the logical
+        caches gathered from its pages."""
+        import types
+        k, v = self.paged_kv(case)
+        return self.prefill_cached(types.SimpleNamespace(q=case.q, k_cache=k, v_cache=v, seq_lens=case.seq_lens,
+                                                         scale=case.scale, causal=case.causal, kv_dtype=case.kv_dtype,
+                                                         k_scale=case.k_scale, v_scale=case.v_scale))
+
     def prefill_rows(self, case, rows, f64=None) -> np.ndarray:
         """Oracle output for selected rows ((b*H + h)*T + i) -> [len(rows), D]."""
         q, k, v = f64 if f64 is not None else (_f64(case.q), _f64(case.k), _f64(case.v))
@@ -343,6 +352,7 @@ def prefill(case): return load().prefill(case)
 def prefill_rows(case, rows, f64=None): return load().prefill_rows(case, rows, f64)
 def prefill_arrays(*a): return load().prefill_arrays(*a)
 def prefill_cached(case): return load().prefill_cached(case)
+def prefill_paged(case): return load().prefill_paged(case)
 def prefill_cached_arrays(*a): return load().prefill_cached_arrays(*a)
 def dequant_e4m3fn(codes, scales): return load().dequant_e4m3fn(codes, scales)
 def e4m3fn_value(code): return load().e4m3fn_value(code)

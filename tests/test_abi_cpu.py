@@ -191,6 +191,28 @@ def test_decode_paged_ignores_kv_capacity(lib):
     assert _paged(lib, kv_capacity=0, num_splits=4, workspace=FAKE, workspace_bytes=16) == WSP
 
 
+def _pchunk(lib, B=2, Tq=16, H=8, G=2, D=128, scale=0.1, causal=1, page_size=16, pps=4, num_pages=8,
+            ptrs=(FAKE,) * 6, **opt):
+    o = gqa.new_opts(**opt)
+    return lib.gqa_prefill_paged(*ptrs, B, Tq, H, G, D, scale, causal, page_size, pps, num_pages, None,
+                                 ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(FAKE, FAKE, FAKE, 0, FAKE, FAKE)), INV),     # no block table
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, 0, FAKE)), INV),     # no seq_lens
+    (dict(page_size=8), INV), (dict(page_size=48), INV), (dict(page_size=1 << 21), INV),
+    (dict(pps=0), INV), (dict(num_pages=0), INV), (dict(Tq=0), INV), (dict(causal=3), INV),
+    (dict(page_size=1 << 20, pps=1 << 12), INV),              # capacity beyond 2^31 rows
+    (dict(path=1), UNS), (dict(path=2), UNS),                 # matrix-core family only
+    (dict(q_dtype=0, kv_dtype=0), UNS), (dict(D=64), UNS), (dict(H=130, G=2), UNS),
+    (dict(kv_dtype=2), INV),                                  # fp8 without scales
+    (dict(kv_dtype=3), UNS),                                  # no INT4 chunks
+])
+def test_prefill_paged_rejects(lib, kw, code):
+    assert _pchunk(lib, **kw) == code
+
+
 def _chunk(lib, B=2, Tq=16, H=8, G=2, D=128, scale=0.1, causal=1, ptrs=(FAKE,) * 5, opts=True, **opt):
     fields = dict(kv_capacity=64)
     fields.update(opt)

@@ -91,3 +91,13 @@ def test_swapped_gather_is_caught(monkeypatch):
         if not np.array_equal(o.decode_paged(W.make_paged(c, 16, seed=7)), o.decode(c), equal_nan=True):
             caught += 1
     assert caught == 2
+
+
+@pytest.mark.parametrize("kvd,ps", [(W.BF16, 16), (W.BF16, 64), (W.FP8, 32)])
+def test_paged_chunk_is_the_contiguous_chunk(kvd, ps):
+    """A chunk against a paged cache gathers the same logical rows: its oracle output equals
+    the contiguous chunk's exactly (padding pages and spare pages hold poison)."""
+    c = W.make_chunk(3, 16, 4, 128, 40, [300, 40, 0], T_cap=320, seed=5, name="pc", kv_dtype=kvd)
+    p = W.make_paged_chunk(c, ps, seed=ps)
+    assert p.T_cap >= c.T_cap
+    np.testing.assert_array_equal(oracle.prefill_paged(p), oracle.prefill_cached(c))

@@ -226,15 +226,9 @@ class PagedDecodeCase:
     def T_cap(self): return self.pages_per_seq * self.page_size
 
 
-def make_paged(case: DecodeCase, page_size: int, seed: int = 0, spare_pages: Optional[int] = None,
-               name: Optional[str] = None) -> PagedDecodeCase:
-    """Scatter a contiguous decode case into shuffled pages of ``page_size`` rows.
-
-    pages_per_seq = ceil(T_cap / page_size); the logical cache is padded to that many whole
-    pages with poison (NaN, or the fp8 NaN code); ``spare_pages`` (default B) extra pages, all
-    poison, join the pool. A ``torch.randperm`` of the pool (generator seeded with ``seed``)
-    gives the physical page of each (sequence, logical page). Scales are unchanged."""
-    B, G, T_cap, D = case.k_cache.shape
+def _page_pools(k_cache, v_cache, page_size: int, seed: int, spare_pages: Optional[int]):
+    """Scatter caches [B, G, T_cap, D] into shuffled pages: returns (k_pool, v_pool, table)."""
+    B, G, T_cap, D = k_cache.shape
     pps = -(-T_cap // page_size)
     spare = B if spare_pages is None else spare_pages
     num_pages = B * pps + spare
@@ -254,10 +248,21 @@ def make_paged(case: DecodeCase, page_size: int, seed: int = 0, spare_pages: Opt
                 pool[int(table[b, p]), :, :rows.shape[1]] = rows
         return pool.view(torch.float8_e4m3fn) if cache.dtype == torch.float8_e4m3fn else pool
 
-    return PagedDecodeCase(name=name or f"{case.name}_paged{page_size}", q=case.q, k_pages=scatter(case.k_cache),
-                           v_pages=scatter(case.v_cache), block_table=table, seq_lens=case.seq_lens,
-                           scale=case.scale, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
-                           k_scale=case.k_scale, v_scale=case.v_scale)
+    return scatter(k_cache), scatter(v_cache), table
+
+
+def make_paged(case: DecodeCase, page_size: int, seed: int = 0, spare_pages: Optional[int] = None,
+               name: Optional[str] = None) -> PagedDecodeCase:
+    """Scatter a contiguous decode case into shuffled pages of ``page_size`` rows.
+
+    pages_per_seq = ceil(T_cap / page_size); the logical cache is padded to that many whole
+    pages with poison (NaN, or the fp8 NaN code); ``spare_pages`` (default B) extra pages, all
+    poison, join the pool. A ``torch.randperm`` of the pool (generator seeded with ``seed``)
+    gives the physical page of each (sequence, logical page). Scales are unchanged."""
+    kp, vp, table = _page_pools(case.k_cache, case.v_cache, page_size, seed, spare_pages)
+    return PagedDecodeCase(name=name or f"{case.name}_paged{page_size}", q=case.q, k_pages=kp, v_pages=vp,
+                           block_table=table, seq_lens=case.seq_lens, scale=case.scale, q_dtype=case.q_dtype,
+                           kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
 
 
 @dataclass
@@ -289,6 +294,50 @@ class ChunkCase:
     def G(self): return self.k_cache.shape[1]
     @property
     def T_cap(self): return self.k_cache.shape[2]
+
+
+@dataclass
+class PagedChunkCase:
+    """A chunk case whose cache rows live in pages (layout as for PagedDecodeCase)."""
+
+    name: str
+    q: torch.Tensor            # [B, H, Tq, D]
+    k_pages: torch.Tensor      # [num_pages, G, page_size, D]
+    v_pages: torch.Tensor
+    block_table: torch.Tensor  # [B, pages_per_seq] int32
+    seq_lens: torch.Tensor     # [B] int32
+    scale: float
+    causal: bool
+    dtype: str
+    kv_dtype: str
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def Tq(self): return self.q.shape[2]
+    @property
+    def D(self): return self.q.shape[3]
+    @property
+    def G(self): return self.k_pages.shape[1]
+    @property
+    def page_size(self): return self.k_pages.shape[2]
+    @property
+    def pages_per_seq(self): return self.block_table.shape[1]
+    @property
+    def T_cap(self): return self.pages_per_seq * self.page_size
+
+
+def make_paged_chunk(case, page_size: int, seed: int = 0, spare_pages: Optional[int] = None,
+                     name: Optional[str] = None) -> PagedChunkCase:
+    """Scatter a contiguous ChunkCase's caches into shuffled pages, as make_paged does."""
+    kp, vp, table = _page_pools(case.k_cache, case.v_cache, page_size, seed, spare_pages)
+    return PagedChunkCase(name=name or f"{case.name}_paged{page_size}", q=case.q, k_pages=kp, v_pages=vp,
+                          block_table=table, seq_lens=case.seq_lens, scale=case.scale, causal=case.causal,
+                          dtype=case.dtype, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
 
 
 def make_chunk(B, H, G, D, Tq, seq_lens, T_cap=None, dtype=BF16, causal=True, seed=0, name="chunk",
