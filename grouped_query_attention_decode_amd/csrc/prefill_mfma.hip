@@ -118,9 +118,10 @@ __device__ __forceinline__ void fetch_tile_f8(i32x4_t (&f)[2], const char *src, 
     }
 }
 // Paged cache (pools [num_pages, G, page_size, D], one block-table row per sequence, read
-// through the scalar cache): the 4 (bf16) or 8 (fp8) rows one load instruction moves start at
-// a multiple of 4 or 8 and pages hold >= 16 rows, so they lie in one page and one buffer
-// resource covers them. Table entries and page ids are clamped into range (memory-safe).
+// through the scalar cache): a wave's 16 rows of a tile start at a multiple of 16 and pages
+// hold >= 16 rows, so they lie in one page -- one table read per wave and tile serves its K
+// and V loads; each load instruction (4 bf16 or 8 fp8 rows) gets a buffer resource covering
+// its valid rows. Table entries and page ids are clamped into range (memory-safe).
 typedef const __attribute__((address_space(4))) int32_t cint32_t;
 struct PageGeo {
     const char *k, *v;  // pools advanced to KV head g
@@ -128,37 +129,41 @@ struct PageGeo {
     cint32_t *bt;       // block-table row of the sequence
     int ps_log2, n_bt, num_pages;
 };
-template <int RB, int ROWS>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const PageGeo &pg, const char *pool, int row0, int L) {
-    int pi = row0 >> pg.ps_log2;
+// Byte offset, inside the pools, of key row `row` (the page of `row` looked up once).
+__device__ __forceinline__ long page_row_base(const PageGeo &pg, int row, int rb) {
+    int pi = row >> pg.ps_log2;
     pi = pi < 0 ? 0 : (pi >= pg.n_bt ? pg.n_bt - 1 : pi);
     int page = __builtin_amdgcn_readfirstlane(pg.bt[pi]);
     page = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
+    return page * pg.page_bytes + (long)(row & ((1 << pg.ps_log2) - 1)) * rb;
+}
+template <int RB, int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char *base, int row0, int L) {
     const int rows = L - row0;
     const int bytes = rows <= 0 ? 0 : (rows < ROWS ? rows : ROWS) * RB;
-    const char *base = pool + page * pg.page_bytes + (long)(row0 & ((1 << pg.ps_log2) - 1)) * RB;
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void load_tile_paged(char *lds_tile, const PageGeo &pg, const char *pool, int k0, int L,
-                                                int wave, TileOffs t) {
+__device__ __forceinline__ void load_tile_paged(char *lds_tile, const char *pool, long wbase, int k0, int L, int wave,
+                                                TileOffs t) {
     char *const dst = lds_tile + wave * 4 * 1024;
-    const int r0 = k0 + 16 * wave;  // first key row of this wave's four instructions
-    // Tile offsets relative to each instruction's first row (4 n rows into the tile).
-    const int n0 = wave * 4 * 4 * kRowBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0, L), GQA_LDS(void, dst), 16,
-                                             t.o0 - n0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 4, L), GQA_LDS(void, dst + 1024),
-                                             16, t.o1 - n0 - 4 * kRowBytes, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 8, L), GQA_LDS(void, dst + 2048),
-                                             16, t.o2 - n0 - 8 * kRowBytes, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc<kRowBytes, 4>(pg, pool, r0 + 12, L), GQA_LDS(void, dst + 3072),
-                                             16, t.o3 - n0 - 12 * kRowBytes, 0, 0, 0);
+    const int r0 = k0 + 16 * wave;        // the wave's first key row; wbase: its offset in the pool
+    const char *src = pool + wbase;
+    const int n0 = wave * 16 * kRowBytes;  // tile offsets -> offsets from each instruction's first row
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc<kRowBytes, 4>(src, r0, L), GQA_LDS(void, dst), 16, t.o0 - n0,
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc<kRowBytes, 4>(src + 4 * kRowBytes, r0 + 4, L),
+                                             GQA_LDS(void, dst + 1024), 16, t.o1 - n0 - 4 * kRowBytes, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc<kRowBytes, 4>(src + 8 * kRowBytes, r0 + 8, L),
+                                             GQA_LDS(void, dst + 2048), 16, t.o2 - n0 - 8 * kRowBytes, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc<kRowBytes, 4>(src + 12 * kRowBytes, r0 + 12, L),
+                                             GQA_LDS(void, dst + 3072), 16, t.o3 - n0 - 12 * kRowBytes, 0, 0, 0);
 }
-__device__ __forceinline__ void fetch_tile_f8_paged(i32x4_t (&f)[2], const PageGeo &pg, const char *pool, int k0, int L,
+__device__ __forceinline__ void fetch_tile_f8_paged(i32x4_t (&f)[2], const char *pool, long wbase, int k0, int L,
                                                     int wave, int lane) {
+    const int r0 = k0 + 16 * wave;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const __amdgpu_buffer_rsrc_t rs = page_rsrc<kRowBytesF8, 8>(pg, pool, k0 + 16 * wave + 8 * i, L);
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc<kRowBytesF8, 8>(pool + wbase + 8 * i * kRowBytesF8, r0 + 8 * i, L);
         f[i] = __builtin_bit_cast(i32x4_t,
                                   __builtin_amdgcn_raw_buffer_load_b128(rs, (lane >> 3) * kRowBytesF8 + 16 * (lane & 7), 0, 0));
     }
@@ -254,8 +259,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
     // Fetch / load the K and V tile starting at key k0 (contiguous or paged).
     auto fetch_f8 = [&](i32x4_t (&kf)[2], i32x4_t (&vf)[2], int k0) __attribute__((always_inline)) {
         if constexpr (PG) {
-            fetch_tile_f8_paged(kf, pgeo, pgeo.k, k0, Lb, wave, lane);
-            fetch_tile_f8_paged(vf, pgeo, pgeo.v, k0, Lb, wave, lane);
+            const long wb = page_row_base(pgeo, k0 + 16 * wave, kRowBytesF8);
+            fetch_tile_f8_paged(kf, pgeo.k, wb, k0, Lb, wave, lane);
+            fetch_tile_f8_paged(vf, pgeo.v, wb, k0, Lb, wave, lane);
         } else {
             fetch_tile_f8(kf, kbase, k0, Lb, wave, lane);
             fetch_tile_f8(vf, vbase, k0, Lb, wave, lane);
@@ -393,8 +399,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(AttnArgs a) {
 
     auto load_kv = [&](char *kl, char *vl, int k0) __attribute__((always_inline)) {
         if constexpr (PG) {
-            load_tile_paged(kl, pgeo, pgeo.k, k0, Lb, wave, toffs);
-            load_tile_paged(vl, pgeo, pgeo.v, k0, Lb, wave, toffs);
+            const long wb = page_row_base(pgeo, k0 + 16 * wave, kRowBytes);
+            load_tile_paged(kl, pgeo.k, wb, k0, Lb, wave, toffs);
+            load_tile_paged(vl, pgeo.v, wb, k0, Lb, wave, toffs);
         } else {
             load_tile(kl, kbase, k0, Lb, wave, toffs);
             load_tile(vl, vbase, k0, Lb, wave, toffs);
