@@ -4,8 +4,9 @@ Each case draws its configuration from a fixed seed: decode (contiguous or paged
 without the fused cache append, forced or automatic splits, uniform or flat layout), prefill
 and chunked prefill; head dims 64 to 128, 1 to 64 query heads per KV head, ragged lengths
 with empty sequences, lengths past the capacity and rows of NaN beyond each length; bf16,
-fp32, fp8 and INT4 caches. A combination the library reports as unsupported is skipped;
-every other result must match the oracle within the tolerance of its cache type.
+fp32, fp8 and INT4 caches. Every combination drawn is a supported one (the flat layout only
+where the matrix-core family runs), and every result must match the oracle within the
+tolerance of its cache type.
 """
 
 import sys
@@ -20,7 +21,6 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {W.F32: 1e-5, W.BF16: 2e-2, W.FP8: 5e-2, W.INT4: 5e-2}
-UNSUPPORTED = 2
 
 
 def _say(msg):
@@ -75,6 +75,8 @@ def decode_case(i):
     paged = kvd != W.F32 and D == 128 and rng.random() < 0.3
     append = not paged and kvd != W.F32 and rng.random() < 0.3
     page = int(rng.choice([16, 32, 64]))
+    if layout == "flat" and (D != 128 or kvd == W.F32):
+        layout = "auto"  # the flat layout belongs to the matrix-core family (D = 128, bf16 q)
     return c, layout, splits, paged, append, page
 
 
@@ -108,9 +110,8 @@ def test_random_decode(gqa, i):
                              k_scale=ks, v_scale=vs, layout=layout, num_splits=splits)
         torch.cuda.synchronize()
     except gqa.GqaError as e:
-        if e.status == UNSUPPORTED:
-            pytest.skip(f"unsupported combination: {e}")
-        raise
+        # every combination drawn here is one the library documents as supported
+        raise AssertionError(f"random decode {i}: {e} (status {e.status})") from e
     _check(out, want, TOL[c.kv_dtype], f"random decode {i}")
 
 
