@@ -179,8 +179,10 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
  * (likewise v). The capacity is pages_per_seq * page_size rows per sequence and replaces
  * opts->kv_capacity; seq_lens are read as in gqa_decode against that capacity. page_size is a
  * power of two from 16 to 2^20. Only the table entries that cover rows 0 .. seq_lens[b]-1 are
- * used for the result; entries outside 0 .. num_pages-1 are clamped into that range (no
- * out-of-bounds access; the result is then unspecified). Pages may be shared or unused.
+ * used for the result (later entries of the row may be read, so all pages_per_seq entries must
+ * be allocated, whatever they hold); entries outside 0 .. num_pages-1 are clamped into that
+ * range (no out-of-bounds access; the result is then unspecified). Pages may be shared or
+ * unused.
  *
  * Every option of gqa_decode applies (dtypes, fp8 scales per (sequence, KV head), workspace
  * of gqa_decode_workspace_size() for kv_capacity = pages_per_seq * page_size, layout, cache
@@ -240,8 +242,9 @@ gqa_status gqa_prefill_cached(const void *q, const void *k_cache, const void *v_
  * block_table[b][t / page_size]; capacity pages_per_seq * page_size replaces
  * opts->kv_capacity). The chunk's rows are written into their pages by the caller first.
  * page_size: a power of two from 16 to 2^20. Only table entries covering rows below
- * seq_lens[b] are read; entries outside [0, num_pages) are clamped (memory-safe, result
- * unspecified). Kernel family: matrix cores only (bf16 q with a bf16 or fp8 cache,
+ * seq_lens[b] are used for the result (later entries of the row may be read, so all
+ * pages_per_seq entries must be allocated); entries outside [0, num_pages) are clamped
+ * (memory-safe, result unspecified). Kernel family: matrix cores only (bf16 q with a bf16 or fp8 cache,
  * D = 128, R up to 64); anything else returns GQA_ERR_UNSUPPORTED.
  */
 gqa_status gqa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
