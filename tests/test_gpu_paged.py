@@ -159,3 +159,24 @@ def test_prefill_paged(gqa, B, H, G, Tq, lens, T_cap, kvd, causal, ps):
     torch.cuda.synchronize()
     check(got, oracle.prefill_paged(p), 5e-2 if kvd == W.FP8 else 2e-2, "prefill_paged")
     assert torch.equal(got.cpu(), flat.cpu()), "paged and contiguous chunks differ"
+
+
+@pytest.mark.parametrize("kvd", [W.BF16, W.FP8])
+def test_prefill_paged_out_of_pool_entries(gqa, kvd):
+    """Chunked prefill: table entries for pages past each sequence's length hold ids outside
+    the pool (clamped, no fault) and do not change the result."""
+    c = W.make_chunk(3, 32, 8, 128, 40, [300, 40, 0], T_cap=320, causal=True, seed=61, name="pchunk_clamp",
+                     kv_dtype=kvd)
+    p = W.make_paged_chunk(c, 16, seed=62)
+    bt = p.block_table.clone()
+    for b, L in enumerate(c.seq_lens.tolist()):
+        used = -(-L // 16)
+        bt[b, used:] = torch.tensor([-7, 1 << 30] * 20, dtype=torch.int32)[:bt.shape[1] - used]
+    d = "cuda"
+    ks = c.k_scale.to(d) if c.k_scale is not None else None
+    vs = c.v_scale.to(d) if c.v_scale is not None else None
+    _say(f"[gpu] prefill_paged out-of-pool table entries kv={kvd}")
+    got = gqa.prefill_paged(p.q.to(d), p.k_pages.to(d), p.v_pages.to(d), bt.to(d), p.seq_lens.to(d),
+                            scale=p.scale, causal=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    check(got, oracle.prefill_paged(p), TOL[kvd], f"prefill_paged clamped table kv={kvd}")
