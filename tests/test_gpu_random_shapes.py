@@ -80,7 +80,7 @@ def decode_case(i):
     return c, layout, splits, paged, append, page
 
 
-@pytest.mark.parametrize("i", range(32))
+@pytest.mark.parametrize("i", range(96))
 def test_random_decode(gqa, i):
     c, layout, splits, paged, append, page = decode_case(i)
     d = "cuda"
@@ -115,7 +115,7 @@ def test_random_decode(gqa, i):
     _check(out, want, TOL[c.kv_dtype], f"random decode {i}")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_random_prefill(gqa, i):
     rng = np.random.default_rng(2000 + i)
     dt = str(rng.choice([W.BF16, W.BF16, W.F32]))
@@ -132,7 +132,7 @@ def test_random_prefill(gqa, i):
     _check(out, oracle.prefill(c), TOL[dt], f"random prefill {i}")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_random_chunk(gqa, i):
     rng = np.random.default_rng(3000 + i)
     D = 128 if rng.random() < 0.7 else 64
