@@ -2,7 +2,7 @@
 
 Each case draws its configuration from a fixed seed: decode (contiguous or paged, with or
 without the fused cache append, forced or automatic splits, uniform or flat layout), prefill
-and chunked prefill; head dims 64 to 128, 1 to 64 query heads per KV head, ragged lengths
+and chunked prefill (contiguous or paged cache); head dims 64 to 128, 1 to 64 query heads per KV head, ragged lengths
 with empty sequences, lengths past the capacity and rows of NaN beyond each length; bf16,
 fp32, fp8 and INT4 caches. Every combination drawn is a supported one (the flat layout only
 where the matrix-core family runs), and every result must match the oracle within the
@@ -143,12 +143,20 @@ def test_random_chunk(gqa, i):
     lens = _lens(rng, B, T_cap)
     causal = bool(rng.random() < 0.7)
     kvd = W.FP8 if rng.random() < 0.25 else W.BF16
+    paged = D == 128 and rng.random() < 0.3
+    page = int(rng.choice([16, 32, 64]))
     c = W.make_chunk(B, H, G, D, Tq, lens, T_cap=T_cap, causal=causal, seed=i, name=f"randc{i}", kv_dtype=kvd)
     d = "cuda"
-    _say(f"[gpu] random chunk {i}: B{B} H{H} G{G} D{D} Tq{Tq} T_cap{T_cap} lens={lens} causal={causal} kv={kvd}")
+    _say(f"[gpu] random chunk {i}: B{B} H{H} G{G} D{D} Tq{Tq} T_cap{T_cap} lens={lens} causal={causal} kv={kvd} "
+         f"paged={paged and page}")
     ks = c.k_scale.to(d) if c.k_scale is not None else None
     vs = c.v_scale.to(d) if c.v_scale is not None else None
-    out = gqa.prefill_cached(c.q.to(d), c.k_cache.to(d), c.v_cache.to(d), c.seq_lens.to(d), scale=c.scale,
-                             causal=causal, k_scale=ks, v_scale=vs)
+    if paged:
+        p = W.make_paged_chunk(c, page, seed=i)
+        out = gqa.prefill_paged(p.q.to(d), p.k_pages.to(d), p.v_pages.to(d), p.block_table.to(d),
+                                p.seq_lens.to(d), scale=p.scale, causal=causal, k_scale=ks, v_scale=vs)
+    else:
+        out = gqa.prefill_cached(c.q.to(d), c.k_cache.to(d), c.v_cache.to(d), c.seq_lens.to(d), scale=c.scale,
+                                 causal=causal, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     _check(out, oracle.prefill_cached(c), TOL[kvd], f"random chunk {i}")
