@@ -94,6 +94,38 @@ static void attend_row(const double *q, const double *K, const double *V, long n
     }
 }
 
+/* Decode's own coding of the same definition (every prefill row goes through attend_row
+ * above): the softmax is normalised through the log of its denominator,
+ * p_t = exp(s_t - lse) with lse = m + log(sum_t exp(s_t - m)), and the output is built one
+ * value row at a time, out += p_t * v_t. In exact arithmetic it equals attend_row; it is
+ * written apart so that the pin "incremental decode equals causal prefill" compares two
+ * codings of the definition, not one with itself. w is caller scratch of at least n doubles;
+ * n <= 0 writes zeros. */
+static void decode_row(const double *q, const double *K, const double *V, long n, int D,
+                       double scale, double *out, double *w)
+{
+    long t;
+    int e;
+    for (e = 0; e < D; ++e) out[e] = 0.0;
+    if (n <= 0) return;
+    double top = -INFINITY;
+    for (t = 0; t < n; ++t) {
+        const double *kt = K + t * (long)D;
+        double qk = 0.0;
+        for (e = 0; e < D; ++e) qk += kt[e] * q[e];
+        w[t] = qk * scale;
+        if (w[t] > top) top = w[t];
+    }
+    double z = 0.0;
+    for (t = 0; t < n; ++t) z += exp(w[t] - top);
+    const double lse = top + log(z);
+    for (t = 0; t < n; ++t) {
+        const double p = exp(w[t] - lse);
+        const double *vt = V + t * (long)D;
+        for (e = 0; e < D; ++e) out[e] += p * vt[e];
+    }
+}
+
 static int kv_head_of(int h, int H, int G) { return h / (H / G); }
 
 int gqa_oracle_num_threads(void)
@@ -137,7 +169,7 @@ int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_ca
                 if (L > T_cap) L = T_cap;
                 const double *K = k_cache + ((long)b * G + g) * T_cap * D;
                 const double *V = v_cache + ((long)b * G + g) * T_cap * D;
-                attend_row(q + bh * D, K, V, L, D, scale, out + bh * D, s);
+                decode_row(q + bh * D, K, V, L, D, scale, out + bh * D, s);
             }
             free(s);
         }
@@ -169,7 +201,7 @@ int gqa_oracle_decode_rows(const double *q, const double *k_cache, const double 
                 if (L > T_cap) L = T_cap;
                 const double *K = k_cache + ((long)b * G + g) * T_cap * D;
                 const double *V = v_cache + ((long)b * G + g) * T_cap * D;
-                attend_row(q + bh * D, K, V, L, D, scale, out_rows + r * D, s);
+                decode_row(q + bh * D, K, V, L, D, scale, out_rows + r * D, s);
             }
             free(s);
         }

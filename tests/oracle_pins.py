@@ -331,13 +331,14 @@ def pin_e4m3fn_encoder(orc):
 
 
 def pin_chunk_special_cases(orc):
-    """Chunked prefill reduces to decode (Tq = 1) and to plain prefill (L = Tq = T_cap), both
-    exactly (same rows, same key counts, same summation order)."""
+    """Chunked prefill reduces to decode (Tq = 1; the decode has its own coding of the softmax,
+    so equal up to rounding) and to plain prefill (L = Tq = T_cap; exactly: same rows, same key
+    counts, same summation order)."""
     B, H, G, D, T = 2, 8, 2, 16, 20
     q, k, v = _rand((B, H, T, D), 201), _rand((B, G, T, D), 202), _rand((B, G, T, D), 203)
     lens = np.array([T, 7], dtype=np.int32)
     one = orc.prefill_cached_arrays(q[:, :, :1], k, v, lens, 0.3, True)[:, :, 0]
-    assert np.array_equal(one, orc.decode_arrays(q[:, :, 0], k, v, lens, 0.3)), "Tq = 1 is decode"
+    _close(one, orc.decode_arrays(q[:, :, 0], k, v, lens, 0.3), 1e-13, "Tq = 1 is decode")
     full = np.full(B, T, dtype=np.int32)
     for causal in (True, False):
         got = orc.prefill_cached_arrays(q, k, v, full, 0.3, causal)
@@ -371,7 +372,7 @@ def pin_chunk_short_cache(orc):
         assert np.array_equal(got[0, h, Tq - L], v[0, h // 2, 0].numpy()), "position 0 sees key 0 only"
     nc = orc.prefill_cached_arrays(q, k, v, lens, 0.5, False)
     for i in range(Tq):
-        assert np.array_equal(nc[:, :, i], orc.decode_arrays(q[:, :, i], k, v, lens, 0.5)), f"row {i}"
+        _close(nc[:, :, i], orc.decode_arrays(q[:, :, i], k, v, lens, 0.5), 1e-13, f"row {i}")
 
 
 def pin_int4_format(orc):

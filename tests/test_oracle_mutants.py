@@ -30,6 +30,13 @@ MUTANTS = [
      "int gqa_oracle_int4_value(int u) { return (u & 15) - 7; }"),
     ("int4_nibble_order", "int u = (i & 1) ? (byte >> 4) : (byte & 15);", "int u = (i & 1) ? (byte & 15) : (byte >> 4);"),
     ("int4_ties_to_odd", "(f == 0.5 && fmod(r, 2.0) != 0.0)", "(f == 0.5 && fmod(r, 2.0) == 0.0)"),
+    # The decode's own coding of the softmax (decode_row).
+    ("decode_dropped_scale", "w[t] = qk * scale;", "w[t] = qk;"),
+    ("decode_softmax_sign", "const double p = exp(w[t] - lse);", "const double p = exp(lse - w[t]);"),
+    ("decode_lse_without_log", "const double lse = top + log(z);", "const double lse = top + z;"),
+    ("decode_lse_without_max", "const double lse = top + log(z);", "const double lse = log(z);"),
+    ("decode_transposed_v", "const double *vt = V + t * (long)D;", "const double *vt = V + t;"),
+    ("decode_skips_last_row", "for (t = 0; t < n; ++t) {\n        const double p", "for (t = 0; t + 1 < n; ++t) {\n        const double p"),
     ("chunk_not_causal_masks", "long n = causal ? (p + 1 < L ? p + 1 : L) : L;", "long n = p + 1 < L ? p + 1 : L;"),
 ]
 
