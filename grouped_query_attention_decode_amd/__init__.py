@@ -142,11 +142,23 @@ def _dtype_code(t: torch.Tensor, what: str) -> int:
     return _TORCH_TO_CODE[t.dtype]
 
 
-def _need_cuda(t: torch.Tensor, what: str):
+def _need_cuda(t: torch.Tensor, what: str, device=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, not on q's device {device}")
+
+
+def _check_out(out, q, what="out"):
+    """A caller's output must have q's device, dtype and shape: the kernels write q.numel()
+    elements of q's type to it."""
+    _need_cuda(out, what, q.device)
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"{what} must be {tuple(q.shape)} {q.dtype} like q, got {tuple(out.shape)} {out.dtype}")
+    if out.data_ptr() == q.data_ptr():
+        raise ValueError(f"{what} must not alias q")
 
 
 def _stream_handle(stream, device) -> int:
@@ -155,30 +167,59 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream)
 
 
-def _decode_opts(q, cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, layout, k_new, v_new, workspace):
+def _on_stream(stream, make):
+    """Run make() with `stream` current, so that memory it allocates belongs to that stream (the
+    caching allocator then never hands it to other work while the call's kernels use it) and the
+    work it enqueues (a zero fill) is ordered before those kernels."""
+    if stream is None:
+        return make()
+    with torch.cuda.stream(stream):
+        return make()
+
+
+def _new_out(q, stream):
+    return _on_stream(stream, lambda: torch.empty_like(q))
+
+
+def _scales(o, B, G, k_scale, v_scale, device, what):
+    if k_scale is None or v_scale is None:
+        raise ValueError(f"{what} need k_scale and v_scale")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need_cuda(t, n, device)
+        if t.dtype != torch.float32 or t.numel() != B * G:
+            raise ValueError(f"{n} must be float32 [B*G]")
+    o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+
+
+def _decode_opts(q, cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, layout, k_new, v_new, workspace,
+                 stream):
+    if path not in PATHS or layout not in LAYOUTS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}, layout one of {sorted(LAYOUTS)}")
     kv_code = _dtype_code(cache, "k_cache")
     o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
                  num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
     if kv_code in (DTYPES["fp8_e4m3fn"], DTYPES["int4"]):
-        if k_scale is None or v_scale is None:
-            raise ValueError("fp8 and INT4 caches need k_scale and v_scale")
-        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
-            _need_cuda(t, n)
-            if t.dtype != torch.float32 or t.numel() != B * G:
-                raise ValueError(f"{n} must be float32 [B*G]")
-        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        _scales(o, B, G, k_scale, v_scale, q.device, "fp8 and INT4 caches")
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
     if k_new is not None:
         for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-            _need_cuda(t, n)
+            _need_cuda(t, n, q.device)
             if t.dtype != q.dtype or tuple(t.shape) != (B, G, D):
                 raise ValueError(f"{n} must be [B, G, D] = {(B, G, D)} in q's dtype")
         o.k_new, o.v_new = k_new.data_ptr(), v_new.data_ptr()
     need = decode_workspace_size(B, q.shape[1], G, D, T_cap, kv_code, int(num_splits))
+    if need == (1 << 64) - 1:
+        raise ValueError("decode sizes out of range")
+    if workspace is not None:
+        _need_cuda(workspace, "workspace", q.device)
+        have = workspace.numel() * workspace.element_size()
+        if have < need:
+            raise ValueError(f"workspace holds {have} bytes, these sizes need {need}")
     if need > 0:
         if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+            # Allocated and zero-filled on the call's stream: ordered before its kernels.
+            workspace = _on_stream(stream, lambda: torch.zeros(need, dtype=torch.uint8, device=q.device))
         o.workspace, o.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return o, workspace
 
@@ -197,8 +238,9 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
     ``workspace`` (uint8 device tensor of at least ``decode_workspace_size`` bytes) must be
     zero-filled before its first use; each completed call leaves it ready for the next.
     Without one, a zeroed workspace is allocated for this call."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
-        _need_cuda(t, n)
+    _need_cuda(q, "q")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n, q.device)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("expected q [B,H,D] and k_cache, v_cache [B,G,T_cap,D]")
     B, H, D = q.shape
@@ -210,12 +252,12 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
     if k_cache.dtype != v_cache.dtype:
         raise TypeError("k_cache and v_cache must share a dtype")
     if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out, "out")
+        out = _new_out(q, stream)
+    _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o, workspace = _decode_opts(q, k_cache, B, G, D, T_cap, k_scale, v_scale, num_splits, path, layout,
-                                k_new, v_new, workspace)
+                                k_new, v_new, workspace, stream)
     st = library().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                               out.data_ptr(), B, H, G, D, float(scale), _stream_handle(stream, q.device),
                               ctypes.byref(o))
@@ -232,9 +274,9 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=Non
     row t of sequence b is row t % page_size of page block_table[b, t // page_size]. The other
     arguments are those of ``decode`` (the workspace size is that of a cache of
     pages_per_seq * page_size rows)."""
-    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
-                 (seq_lens, "seq_lens")):
-        _need_cuda(t, n)
+    _need_cuda(q, "q")
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n, q.device)
     if q.dim() != 3 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
         raise ValueError("expected q [B,H,D], pools [num_pages,G,page_size,D] and block_table [B,pages_per_seq]")
     B, H, D = q.shape
@@ -248,12 +290,12 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=Non
     if k_pages.dtype != v_pages.dtype:
         raise TypeError("k_pages and v_pages must share a dtype")
     if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out, "out")
+        out = _new_out(q, stream)
+    _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o, workspace = _decode_opts(q, k_pages, B, G, D, pages_per_seq * page_size, k_scale, v_scale, num_splits,
-                                path, layout, k_new, v_new, workspace)
+                                path, layout, k_new, v_new, workspace, stream)
     st = library().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                                     seq_lens.data_ptr(), out.data_ptr(), B, H, G, D, float(scale), page_size,
                                     pages_per_seq, num_pages, _stream_handle(stream, q.device), ctypes.byref(o))
@@ -264,17 +306,22 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=Non
 
 def prefill(q, k, v, out=None, scale=None, causal=True, path="auto", stream=None):
     """GQA prefill (causal by default). Returns ``out`` [B, H, T, D] (q's dtype)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need_cuda(t, n)
+    _need_cuda(q, "q")
+    for t, n in ((k, "k"), (v, "v")):
+        _need_cuda(t, n, q.device)
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("expected q [B,H,T,D] and k, v [B,G,T,D]")
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
     B, H, T, D = q.shape
     Bk, G, Tk, Dk = k.shape
     if (Bk, Tk, Dk) != (B, T, D):
         raise ValueError("shape mismatch between q and k/v")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
     if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out, "out")
+        out = _new_out(q, stream)
+    _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=_dtype_code(k, "k"), path=PATHS[path])
@@ -287,16 +334,12 @@ def prefill(q, k, v, out=None, scale=None, causal=True, path="auto", stream=None
 
 
 def _chunk_opts(q, cache, B, G, T_cap, k_scale, v_scale, path):
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
     kv_code = _dtype_code(cache, "cache")
     o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap, path=PATHS[path])
     if kv_code == DTYPES["fp8_e4m3fn"]:
-        if k_scale is None or v_scale is None:
-            raise ValueError("fp8 caches need k_scale and v_scale")
-        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
-            _need_cuda(t, n)
-            if t.dtype != torch.float32 or t.numel() != B * G:
-                raise ValueError(f"{n} must be float32 [B*G]")
-        o.k_scale, o.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        _scales(o, B, G, k_scale, v_scale, q.device, "fp8 caches")
     return o
 
 
@@ -306,8 +349,9 @@ def prefill_cached(q, k_cache, v_cache, seq_lens, out=None, scale=None, causal=T
 
     q [B, H, Tq, D]; caches [B, G, T_cap, D] already holding the chunk's keys and values at rows
     seq_lens[b]-Tq .. seq_lens[b]-1; query i of sequence b sits at position seq_lens[b]-Tq+i."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
-        _need_cuda(t, n)
+    _need_cuda(q, "q")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n, q.device)
     if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("expected q [B,H,Tq,D] and k_cache, v_cache [B,G,T_cap,D]")
     B, H, Tq, D = q.shape
@@ -317,8 +361,8 @@ def prefill_cached(q, k_cache, v_cache, seq_lens, out=None, scale=None, causal=T
     if k_cache.dtype != v_cache.dtype:
         raise TypeError("k_cache and v_cache must share a dtype")
     if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out, "out")
+        out = _new_out(q, stream)
+    _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = _chunk_opts(q, k_cache, B, G, T_cap, k_scale, v_scale, path)
@@ -336,9 +380,9 @@ def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=No
 
     ``k_pages``/``v_pages`` [num_pages, G, page_size, D] and ``block_table`` int32 [B, pages_per_seq]
     as for ``decode_paged``; the other arguments are those of ``prefill_cached``."""
-    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
-                 (seq_lens, "seq_lens")):
-        _need_cuda(t, n)
+    _need_cuda(q, "q")
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n, q.device)
     if q.dim() != 4 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
         raise ValueError("expected q [B,H,Tq,D], pools [num_pages,G,page_size,D] and block_table [B,pages_per_seq]")
     B, H, Tq, D = q.shape
@@ -350,8 +394,8 @@ def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, scale=No
     if k_pages.dtype != v_pages.dtype:
         raise TypeError("k_pages and v_pages must share a dtype")
     if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out, "out")
+        out = _new_out(q, stream)
+    _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = _chunk_opts(q, k_pages, B, G, pages_per_seq * page_size, k_scale, v_scale, path)

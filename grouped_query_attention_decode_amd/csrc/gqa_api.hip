@@ -326,10 +326,15 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     void *ws = o.workspace;
     bool owned = false;
     if (need > 0 && !ws) {
+        // Stream-ordered memory of this call's own. Not while the stream is being captured into
+        // a graph: the allocation and its release would become graph nodes.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return GQA_ERR_HIP;
+        if (cap != hipStreamCaptureStatusNone) return GQA_ERR_WORKSPACE;
         if (hipMallocAsync(&ws, need, stream) != hipSuccess) return GQA_ERR_HIP;
         owned = true;
         // Fresh memory: the arrival counters must start at zero.
-        if (hipMemsetAsync(ws, 0, counter_bytes(B, G), stream) != hipSuccess) {
+        if (launch_zero_ints(static_cast<int *>(ws), B * G, stream) != hipSuccess) {
             (void)hipFreeAsync(ws, stream);
             return GQA_ERR_HIP;
         }

@@ -50,6 +50,7 @@ hipError_t launch_decode_valu(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_kv_append(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_zero_ints(int *p, int n, hipStream_t stream);
 
 // Shape limits of the fast kernels (checked on the host before launch).
 bool decode_valu_supports(const AttnArgs &a);

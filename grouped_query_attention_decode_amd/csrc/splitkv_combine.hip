@@ -169,7 +169,20 @@ __global__ __launch_bounds__(256) void splitkv_combine4_kernel(AttnArgs a) {
     }
 }
 
+// Zero-fill of n ints (the split arrival counters of fresh workspace memory). A kernel rather
+// than hipMemsetAsync, so that the stream carries only kernel work.
+__global__ __launch_bounds__(256) void zero_ints_kernel(int *p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_ints(int *p, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const AttnArgs &a, hipStream_t stream) {
     if (a.D > 256) return hipErrorInvalidValue;

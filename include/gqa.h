@@ -128,16 +128,19 @@ void gqa_opts_init(gqa_opts *opts);
  * The caller has already written the current token's k and v at row seq_lens[b]-1
  * ("LLM principles -- code ...", sections 3 and 5 concatenate the new K/V to the
  * cache before forming scores), so query head h of sequence b attends to rows
- * 0 .. seq_lens[b]-1 of KV head h / (H/G), itself included; rows at or beyond
- * seq_lens[b] are never read. seq_lens lives on the device and is not checked on
- * the host: a value above T_cap is treated as T_cap, a value <= 0 yields a zero
- * output row.
+ * 0 .. seq_lens[b]-1 of KV head h / (H/G), itself included. Rows at or beyond
+ * seq_lens[b] (up to T_cap - 1) may be read but never affect the result, whatever they
+ * hold, NaN included; nothing past T_cap is read. seq_lens lives on the device and is not
+ * checked on the host: a value above T_cap is treated as T_cap, a value <= 0 yields a
+ * zero output row.
  *
  * Long caches are split into num_splits key ranges whose partial results are merged
  * by a log-sum-exp combine ["GQA revolution ...", section on split-KV block
  * computation]; that needs device scratch: opts->workspace of at least
  * gqa_decode_workspace_size() bytes, or NULL to let the call take stream-ordered
- * memory with hipMallocAsync/hipFreeAsync on `stream`. A caller workspace must be
+ * memory with hipMallocAsync/hipFreeAsync on `stream` (zero-filled by a kernel on the same
+ * stream). A NULL workspace is refused with GQA_ERR_WORKSPACE while `stream` is being
+ * captured into a graph: pass a workspace there. A caller workspace must be
  * zero-filled before its first use (it holds per-(sequence, KV head) arrival counters);
  * every completed call leaves it ready for the next one. Calls that run concurrently must
  * not share a workspace.
