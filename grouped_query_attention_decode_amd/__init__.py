@@ -21,7 +21,7 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
-__all__ = ["decode", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "status_string",
+__all__ = ["decode", "decode_noalloc", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
@@ -88,6 +88,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_opts_init.restype = None
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_decode.restype = i
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, ctypes.POINTER(GqaOpts)]
+    lib.gqa_decode_noalloc.restype = i
     lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, ctypes.POINTER(GqaOpts)]
     lib.gqa_decode_paged.restype = i
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, vp, ctypes.POINTER(GqaOpts)]
@@ -263,6 +265,50 @@ def decode(q, k_cache, v_cache, seq_lens, out=None, scale=None, k_scale=None, v_
                               ctypes.byref(o))
     if st != GQA_OK:
         raise GqaError(st, "gqa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, out, scale=None, k_scale=None, v_scale=None, num_splits=0,
+                   path="auto", stream=None, layout="auto", k_new=None, v_new=None):
+    """``decode`` through gqa_decode_noalloc: split partials in the library's static device
+    scratch instead of a workspace, so nothing is allocated (``out`` must be given). Calls that
+    overlap in time on one GPU race on that scratch; calls ordered on one stream do not."""
+    _need_cuda(q, "q")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need_cuda(t, n, q.device)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [B,H,D] and k_cache, v_cache [B,G,T_cap,D]")
+    B, H, D = q.shape
+    Bk, G, T_cap, Dk = k_cache.shape
+    if k_cache.dtype == torch.uint8:
+        Dk *= 2
+    if Bk != B or Dk != D or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens (int32 [B])")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share a dtype")
+    _check_out(out, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if path not in PATHS or layout not in LAYOUTS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}, layout one of {sorted(LAYOUTS)}")
+    kv_code = _dtype_code(k_cache, "k_cache")
+    o = new_opts(q_dtype=_dtype_code(q, "q"), kv_dtype=kv_code, kv_capacity=T_cap,
+                 num_splits=int(num_splits), path=PATHS[path], layout=LAYOUTS[layout])
+    if kv_code in (DTYPES["fp8_e4m3fn"], DTYPES["int4"]):
+        _scales(o, B, G, k_scale, v_scale, q.device, "fp8 and INT4 caches")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _need_cuda(t, n, q.device)
+            if t.dtype != q.dtype or tuple(t.shape) != (B, G, D):
+                raise ValueError(f"{n} must be [B, G, D] = {(B, G, D)} in q's dtype")
+        o.k_new, o.v_new = k_new.data_ptr(), v_new.data_ptr()
+    st = library().gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                      out.data_ptr(), B, H, G, D, float(scale), _stream_handle(stream, q.device),
+                                      ctypes.byref(o))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_decode_noalloc")
     return out
 
 

@@ -188,6 +188,37 @@ gqa_status check_device() {
     return g_arch_ok[dev] == 1 ? GQA_OK : GQA_ERR_UNSUPPORTED;
 }
 
+// ---- Device scratch of gqa_decode_noalloc ----
+// One array per GPU, in the library's own code object, held until the process ends: a fixed
+// region of split arrival counters (only ever used as counters, so the invariant that a
+// completed call leaves them at zero holds across calls of any size), then the split partials.
+// In host code `scratch` names a host-side stand-in, not device memory: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+constexpr int kScratchCounters = 65536;                     // B * G at most
+constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(int);
+constexpr size_t kScratchPartialBytes = size_t(32) << 20;   // 32 MiB of split partials at most
+static __device__ __align__(256) char scratch[kScratchCounterBytes + kScratchPartialBytes];
+
+std::mutex g_scratch_mu;
+char *g_scratch[kNumDevicesMax];  // device address of `scratch`, per device; null until set up
+
+// The current device's scratch: on its first use on a device, look up the array's address there
+// and zero its counters on `stream` (ordered before the call's kernels on that stream).
+gqa_status device_scratch(hipStream_t stream, char **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GQA_ERR_HIP;
+    if (dev < 0 || dev >= kNumDevicesMax) return GQA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GQA_ERR_HIP;
+        if (launch_zero_ints(static_cast<int *>(p), kScratchCounters, stream) != hipSuccess) return GQA_ERR_HIP;
+        g_scratch[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch[dev];
+    return GQA_OK;
+}
+
 }  // namespace
 
 }  // namespace gqa
@@ -249,9 +280,11 @@ struct PagedDesc {
     int page_size, pages_per_seq, num_pages;
 };
 
+// use_scratch: the allocation-free variant (split partials in the library's static device
+// scratch; opts->workspace must be NULL).
 gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *out,
                        int B, int H, int G, int D, float scale, hipStream_t stream, const gqa_opts *opts_in,
-                       const PagedDesc *pg) {
+                       const PagedDesc *pg, bool use_scratch = false) {
     // ---- host-side validation (no HIP calls) ----
     if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts_in) return GQA_ERR_INVALID_ARG;
     gqa_opts o;
@@ -318,6 +351,11 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     const size_t need = workspace_bytes_for(B, H, G, D, a.num_splits);
     if (need > 0 && o.workspace && o.workspace_bytes < need) return GQA_ERR_WORKSPACE;
     if (need > 0 && o.workspace && ((uintptr_t)o.workspace % 16) != 0) return GQA_ERR_INVALID_ARG;
+    if (use_scratch) {
+        if (o.workspace) return GQA_ERR_INVALID_ARG;
+        const size_t part = need > 0 ? need - counter_bytes(B, G) : 0;
+        if (need > 0 && ((long)B * G > kScratchCounters || part > kScratchPartialBytes)) return GQA_ERR_WORKSPACE;
+    }
 
     // ---- device work ----
     gqa_status st = check_device();
@@ -325,7 +363,15 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
 
     void *ws = o.workspace;
     bool owned = false;
-    if (need > 0 && !ws) {
+    if (need > 0 && use_scratch) {
+        char *base = nullptr;
+        st = device_scratch(stream, &base);
+        if (st != GQA_OK) return st;
+        a.counters = reinterpret_cast<int *>(base);
+        a.part_acc = reinterpret_cast<float *>(base + kScratchCounterBytes);
+        a.part_ml = reinterpret_cast<float *>(base + kScratchCounterBytes + acc_bytes(B, H, D, a.num_splits));
+        a.fuse_combine = plan.fuse;
+    } else if (need > 0 && !ws) {
         // Stream-ordered memory of this call's own. Not while the stream is being captured into
         // a graph: the allocation and its release would become graph nodes.
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -339,7 +385,7 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
             return GQA_ERR_HIP;
         }
     }
-    if (need > 0) {
+    if (need > 0 && !use_scratch) {
         char *base = static_cast<char *>(ws);
         a.counters = reinterpret_cast<int *>(base);
         a.part_acc = reinterpret_cast<float *>(base + counter_bytes(B, G));
@@ -442,6 +488,12 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
                       void *out, int B, int H, int G, int D, float scale, hipStream_t stream,
                       const gqa_opts *opts) {
     return gqa::decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, G, D, scale, stream, opts, nullptr);
+}
+
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                              void *out, int B, int H, int G, int D, float scale, hipStream_t stream,
+                              const gqa_opts *opts) {
+    return gqa::decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, G, D, scale, stream, opts, nullptr, true);
 }
 
 gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,

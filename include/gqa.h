@@ -168,6 +168,28 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       float scale, hipStream_t stream, const gqa_opts *opts);
 
 /*
+ * gqa_decode for callers that cannot allocate device memory during the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same arguments,
+ * kernels and results as gqa_decode, except that the split partials and arrival counters live
+ * in a static device array inside libgqa.so instead of a workspace. opts->workspace must be
+ * NULL (else GQA_ERR_INVALID_ARG). The call allocates nothing: no hipMalloc, hipMallocAsync or
+ * hipFree, and no memset.
+ *
+ * Limits: B * G <= 65536, and at most 32 MiB of split partials (gqa_decode_workspace_size()
+ * minus the counter bytes bounds what a call needs); larger calls return GQA_ERR_WORKSPACE
+ * before any HIP call. Each GPU the library runs on holds its own 32.25 MiB array until the
+ * process ends. The first call on a device looks up the array's address there and zero-fills
+ * its counters on `stream`; every completed call leaves them at zero again.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's partials: calls
+ * that overlap in time on one GPU (on different streams, or from different threads without
+ * ordering) race and may give wrong results. Calls ordered on one stream are safe.
+ */
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *seq_lens, void *out, int B, int H, int G, int D,
+                              float scale, hipStream_t stream, const gqa_opts *opts);
+
+/*
  * Single-token decode over a paged KV cache: the same computation as gqa_decode, with the
  * cache rows of each sequence held in fixed-size pages that a block table maps ["GQA
  * revolution ...", section on split-KV block computation, whose work-split heuristic takes a

@@ -100,6 +100,25 @@ def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
+def _decode_noalloc(lib, B=2, H=8, G=2, D=128, scale=0.1, ptrs=(FAKE,) * 5, **opt):
+    fields = dict(kv_capacity=64)
+    fields.update(opt)
+    o = gqa.new_opts(**fields)
+    return lib.gqa_decode_noalloc(*ptrs, B, H, G, D, scale, None, ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=(0, FAKE, FAKE, FAKE, FAKE)), INV),
+    (dict(H=8, G=3), INV),
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=1 << 30), INV),   # the variant takes no workspace
+    (dict(B=70000, H=1, G=1, num_splits=2), WSP),                         # more counters than the scratch holds
+    (dict(B=64, H=64, G=8, kv_capacity=32768, num_splits=64), WSP),       # split partials beyond 32 MiB
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    """The allocation-free variant checks its limits on the host, before any HIP call."""
+    assert _decode_noalloc(lib, **kw) == code
+
+
 def test_decode_requires_opts(lib):
     assert lib.gqa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 128, 0.1, None, None) == INV
 
