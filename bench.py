@@ -2,25 +2,34 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-breakdown]
+    python bench.py --summarize-trace KERNEL_TRACE.csv --steps K
+    python bench.py --summarize-counters FETCH.csv WRITE.csv --steps K --workload NAME
+    python bench.py --summarize-calibration FETCH.csv WRITE.csv
+    python bench.py --copy-calibration
 
 A step is one call of the hot path over one batch of synthetic inputs (seeded, from
-workloads.py). The headline workload is the Llama-2-7B-shaped GQA-8 decode (B1 H32 G8
-D128, 2048 cached tokens, bf16); the others (70B-shaped ragged decode, causal prefill
-B4 T2048, 32k-token fp8 MQA decode) are reported in "breakdown", and so are the headline
-and fp8 decodes with the current token's KV-cache append done by the same call ("+append"),
-three decodes over a cache in shuffled 16-row pages ("_paged16"), two decodes over INT4
-caches, and a prefill of the last
-512 positions of 4096-token sequences against the cache of the first 3584.
+workloads.py). The headline is the largest decode: the Llama-2-70B-shaped GQA-8 decode of a
+ragged batch (B16 H64 G8 D128, lengths drawn from [1024, 4096], bf16); the causal prefill
+(B4 H32 G8 D128 T2048, bf16) is the required second entry ("prefill"). The rest go in
+"breakdown": the Llama-2-7B-shaped decode, the 32k-token fp8 MQA decode, decodes with the
+current token's cache append done by the same call ("+append"), decodes over a cache in
+shuffled 16-row pages ("_paged16"), decodes over INT4 caches, and prefills of the last 512
+positions of 4096-token sequences against the cache of the first 3584.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
-synchronisations. Each step reads the next of several replicas of its inputs, together
-at least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set and the
-figures are HBM figures. The K timed steps are captured once into a HIP graph and
-replayed, so the host's launch cost does not idle the GPU; HIP events on the launch
-stream around the replay give the per-step (= per-launch) duration used for the
-roofline. The eager, host-launched per-call time is reported beside it.
+synchronisations. Each step reads the next of several replicas of its inputs, together at
+least 1 GiB, and a plain streaming read of another 1 GiB (gqa_hbm_stream_read) runs before
+the timed steps, so the 256 MB Infinity Cache holds none of their data whatever K is: the
+figures are HBM figures. The K timed steps are captured once into a HIP graph and replayed,
+so the host's launch cost does not idle the GPU; HIP events on the launch stream around the
+replay give the per-step (= per-launch) duration used for the roofline. The eager,
+host-launched per-call time is reported beside it.
 
-Prints one JSON line.
+The fp64 oracle is timed on the host cores beside the GPU (the headline decode, the causal
+prefill and the fp8 MQA decode), with the core count and CPU model.
+
+Prints one JSON line. The --summarize-* modes turn rocprofv3 output of such a run into the
+summaries kept under profiles/ (the timed dispatches only: the last K of each kernel).
 """
 
 from __future__ import annotations
@@ -47,7 +56,8 @@ COLD_BYTES = 1 << 30            # replicas rotate through at least this much mem
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "grouped_query_attention_decode_amd", "csrc")
 
-HEADLINE = "llama7b_gqa8_decode_L2048"
+HEADLINE = "llama70b_gqa8_decode_B16_ragged"
+PREFILL = "gqa8_causal_prefill_B4_T2048"
 METRIC = "GQA decode KV-read GB/s (% HBM peak) + tok/s; prefill TFLOP/s (% MFMA peak)"
 
 
@@ -188,7 +198,7 @@ def chunk_flops(c: W.ChunkCase) -> int:
     return 4 * c.H * c.D * pairs
 
 
-def bench_chunk(gqa, c, steps, warmup, dev):
+def bench_chunk(gqa, c, steps, warmup, dev, flush):
     """A ChunkCase (contiguous cache) or a PagedChunkCase (its cache in pages)."""
     paged = isinstance(c, W.PagedChunkCase)
     kc, vc = (c.k_pages, c.v_pages) if paged else (c.k_cache, c.v_cache)
@@ -211,7 +221,7 @@ def bench_chunk(gqa, c, steps, warmup, dev):
         else:
             gqa.prefill_cached(q, k, v, lens, out=out, scale=c.scale, causal=c.causal, k_scale=ks, v_scale=vs)
 
-    t = time_steps(step, steps, warmup)
+    t = time_steps(step, steps, warmup, flush)
     fl = chunk_flops(c)
     s = t["ms_per_step"] * 1e-3
     achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -244,8 +254,23 @@ def make_prefill_runner(gqa, c: W.PrefillCase, dev):
     return step, nrep, out
 
 
-def time_steps(step, steps, warmup, graph=True):
-    """Time exactly `steps` calls of `step` after `warmup` untimed calls.
+class Flusher:
+    """Evicts the Infinity Cache (and the L2s) before a timed region: a plain streaming read of
+    a 1 GiB buffer (gqa_hbm_stream_read), four times the 256 MB cache, on the current stream."""
+
+    def __init__(self, gqa, dev, nbytes=1 << 30):
+        self.gqa = gqa
+        self.buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.gqa.hbm_stream_read(self.buf, self.sink)
+        torch.cuda.synchronize()
+
+
+def time_steps(step, steps, warmup, flush, graph=True):
+    """Time exactly `steps` calls of `step` after `warmup` untimed calls, cold: `flush` empties
+    the caches right before each timed region, and every call reads its own input replica.
 
     With graph=True the timed calls are captured once into a HIP graph (each call still
     reads its own input replica) and the graph is replayed between two device
@@ -258,6 +283,7 @@ def time_steps(step, steps, warmup, graph=True):
     torch.cuda.synchronize()
     # Eager per-call time (host launch cost included), for reference.
     n_eager = min(steps, 50)
+    flush()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(n_eager):
@@ -277,6 +303,7 @@ def time_steps(step, steps, warmup, graph=True):
         torch.cuda.synchronize()
         g.replay()  # untimed replay: graph upload, first-touch effects
         torch.cuda.synchronize()
+        flush()
         t_begin = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
@@ -292,7 +319,7 @@ def time_steps(step, steps, warmup, graph=True):
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         t_begin = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        flush()
         t_begin.record()
         for i in range(steps):
             starts[i].record()
@@ -306,9 +333,9 @@ def time_steps(step, steps, warmup, graph=True):
     return res
 
 
-def bench_decode(gqa, c, steps, warmup, dev, append=False):
+def bench_decode(gqa, c, steps, warmup, dev, flush, append=False):
     step, nrep, _ = make_decode_runner(gqa, c, dev, append)
-    t = time_steps(step, steps, warmup)
+    t = time_steps(step, steps, warmup, flush)
     by = decode_bytes(c, append)
     s = t["ms_per_step"] * 1e-3
     launch = t["launch_ms_mean"] * 1e-3
@@ -328,9 +355,9 @@ def bench_decode(gqa, c, steps, warmup, dev, append=False):
     }
 
 
-def bench_prefill(gqa, c, steps, warmup, dev):
+def bench_prefill(gqa, c, steps, warmup, dev, flush):
     step, nrep, _ = make_prefill_runner(gqa, c, dev)
-    t = time_steps(step, steps, warmup)
+    t = time_steps(step, steps, warmup, flush)
     fl = prefill_flops(c)
     s = t["ms_per_step"] * 1e-3
     launch = t["launch_ms_mean"] * 1e-3
@@ -345,54 +372,210 @@ def bench_prefill(gqa, c, steps, warmup, dev):
     }
 
 
-def hbm_achievable(dev, nbytes=1 << 30, reps=5):
-    """What a plain streaming kernel reaches on this device (context beside the published
-    peak): a device copy that reads and writes nbytes, median of reps."""
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+def hbm_achievable(gqa, flusher, reps=11):
+    """What plain streaming reaches on this device, beside the published peak: the in-tree
+    streaming-read kernel (gqa_hbm_stream_read) over a 1 GiB buffer, four times the Infinity
+    Cache, so every launch reads from HBM; median of `reps` launches timed with HIP events on
+    the launch stream. A 1 GiB torch device copy is reported beside it (read + write)."""
+    buf, sink = flusher.buf, flusher.sink
+    nbytes = buf.numel() * buf.element_size()
+    gqa.hbm_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gqa.hbm_stream_read(buf, sink)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    read_gbs = nbytes / sorted(times)[len(times) // 2] / 1e9
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=buf.device)
     dst = torch.empty_like(src)
-    res = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),):
-        fn()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b) * 1e-3)
-        res[f"{name}_GBps"] = moved / sorted(times)[len(times) // 2] / 1e9
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ctimes = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ctimes.append(a.elapsed_time(b) * 1e-3)
     del src, dst
     torch.cuda.empty_cache()
-    res["bytes"] = nbytes
-    res["note"] = "torch device copy of 1 GiB fp32; GB/s counts bytes read plus bytes written"
-    return res
+    return {"read_GBps": read_gbs, "read_frac_of_peak": read_gbs / HBM_PEAK_GBS,
+            "copy_GBps": 2 * nbytes / sorted(ctimes)[len(ctimes) // 2] / 1e9, "bytes": nbytes,
+            "note": "read: gqa_hbm_stream_read (in-tree plain streaming-read kernel), median of "
+                    f"{reps} launches over 1 GiB; copy: torch device copy of 1 GiB, bytes read plus written"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_time(fn, budget_s, max_runs, min_runs=1):
+    times = []
+    t_stop = time.perf_counter() + budget_s
+    while len(times) < min_runs or (time.perf_counter() < t_stop and len(times) < max_runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    return times[len(times) // 2], len(times)
 
 
 def cpu_baseline_decode(c: W.DecodeCase, budget_s=10.0):
-    """The fp64 oracle on the host cores, on the same decode step (whole step, repeated)."""
+    """The fp64 oracle as it stands, on the host cores, on the whole decode step (repeated for
+    about budget_s seconds, median)."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     oracle.set_num_threads(threads)
     k, v = oracle.decode_kv_f64(c)
     q = oracle.to_f64(c.q)
     lens = c.seq_lens.numpy()
-    times = []
-    t_stop = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        oracle.decode_arrays(q, k, v, lens, c.scale)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_stop or len(times) >= 2000:
-            break
-    times.sort()
-    med = times[len(times) // 2]
+    med, n = _median_time(lambda: oracle.decode_arrays(q, k, v, lens, c.scale), budget_s, 2000)
     by = decode_bytes(c)
     return {"value": by["kv"] / med / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"whole {c.name} decode step (fp64 C oracle, OpenMP), median of {len(times)} runs; "
-                      f"{med * 1e3:.2f} ms per step, {c.B / med:.1f} tok/s",
-            "seconds_per_step": med}
+            "sample": f"the whole {c.name} decode step (fp64 C oracle, OpenMP over (b, h) rows), median of {n} "
+                      f"runs; {med * 1e3:.2f} ms per step, {c.B / med:.1f} tok/s",
+            "seconds_per_step": med, "gflops": decode_flops(c) / med / 1e9, "cpu_model": cpu_model()}
+
+
+def cpu_baseline_prefill(c: W.PrefillCase, runs=3):
+    """The fp64 oracle as it stands, on the host cores, on a bounded sample of the prefill: the
+    first sequence of the batch (all H heads, all T rows), median of `runs` runs; the per-step
+    time is that times B (the sequences are independent and equal in work)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(threads)
+    q, k, v = oracle.to_f64(c.q[:1]), oracle.to_f64(c.k[:1]), oracle.to_f64(c.v[:1])
+    med, n = _median_time(lambda: oracle.prefill_arrays(q, k, v, c.scale, c.causal), 0.0, runs, min_runs=runs)
+    fl = prefill_flops(c) / c.B
+    step_s = med * c.B
+    return {"value": fl / med / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"sequence 0 of {c.name} (1 of {c.B}: {c.H} heads x {c.T} causal rows, "
+                      f"{fl / 1e9:.1f} GFLOP), fp64 C oracle with OpenMP over rows, median of {n} runs of "
+                      f"{med:.2f} s; whole step {step_s:.2f} s",
+            "seconds_per_step": step_s, "gflops": fl / med / 1e9, "cpu_model": cpu_model()}
+
+
+def _with_ratio(cpu, gpu_value):
+    if cpu is not None:
+        cpu["gpu_over_oracle"] = gpu_value / cpu["value"] if cpu["value"] > 0 else None
+    return cpu
+
+
+# ------------------------------------------------------------------------------------
+# Summaries of rocprofv3 output (the files kept under profiles/).
+# ------------------------------------------------------------------------------------
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _kernel_name(row):
+    return row.get("Kernel_Name") or row.get("KernelName") or row.get("Name") or "?"
+
+
+def summarize_trace(path, steps):
+    """Per kernel: the last `steps` dispatches of a rocprofv3 --kernel-trace CSV, which in a
+    bench.py run are those of the timed graph replay (warm-up, eager and untimed-replay calls
+    come before it; the cache-flush kernel is listed apart)."""
+    rows = _read_csv(path)
+    by = {}
+    for r in rows:
+        start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        did = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+        by.setdefault(_kernel_name(r), []).append((start, did, (end - start) * 1e-3))
+    out = {}
+    for name, recs in by.items():
+        recs.sort()
+        d = [x[2] for x in recs]
+        last = sorted(d[-steps:])
+        out[name] = {"dispatches": len(d), "timed": len(last), "median_us": last[len(last) // 2],
+                     "mean_us": sum(last) / len(last), "min_us": last[0], "max_us": last[-1]}
+    return out
+
+
+def _counter_per_dispatch(path, counter):
+    rows = _read_csv(path)
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (_kernel_name(r), int(r.get("Dispatch_Id") or r.get("Correlation_Id")))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (name, did), v in sorted(per.items(), key=lambda kv: kv[0][1]):
+        by.setdefault(name, []).append(v)
+    return by
+
+
+def summarize_counters(fetch_csv, write_csv, steps):
+    """Median FETCH_SIZE / WRITE_SIZE (KiB) per kernel over its last `steps` dispatches."""
+    f, w = _counter_per_dispatch(fetch_csv, "FETCH_SIZE"), _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    out = {}
+    for name in f:
+        fl, wl = sorted(f[name][-steps:]), sorted(w.get(name, [0.0])[-steps:])
+        out[name] = {"fetch_kib_median": fl[len(fl) // 2], "write_kib_median": wl[len(wl) // 2]}
+    return out
+
+
+def _summaries(args):
+    """The --summarize-* modes: read rocprofv3 CSV output, print (and for counters record) the
+    figures kept under profiles/. No GPU needed."""
+    if args.summarize_trace:
+        res = summarize_trace(args.summarize_trace, args.steps)
+        print(f"{'kernel':58s} {'disp':>5s} {'timed':>5s} {'median_us':>10s} {'mean_us':>9s} {'min_us':>8s} {'max_us':>8s}")
+        for name, r in sorted(res.items(), key=lambda kv: -kv[1]["median_us"] * kv[1]["timed"]):
+            print(f"{name[:58]:58s} {r['dispatches']:5d} {r['timed']:5d} {r['median_us']:10.2f} {r['mean_us']:9.2f} "
+                  f"{r['min_us']:8.2f} {r['max_us']:8.2f}")
+        return
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {"copy_calibration": None, "workloads": {}}
+    if args.summarize_calibration:
+        fetch_csv, write_csv = args.summarize_calibration
+        res = summarize_counters(fetch_csv, write_csv, 5)
+        name = max(res, key=lambda n: res[n]["fetch_kib_median"])
+        copy_bytes = 1 << 30
+        rec["copy_calibration"] = {
+            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+                       "--copy-calibration",
+            "kernel": name, "copy_bytes": copy_bytes,
+            "fetch_scale": copy_bytes / (res[name]["fetch_kib_median"] * 1024),
+            "write_scale": copy_bytes / (res[name]["write_kib_median"] * 1024)}
+        print(json.dumps(rec["copy_calibration"]))
+    else:
+        fetch_csv, write_csv = args.summarize_counters
+        cal = rec.get("copy_calibration")
+        if not cal:
+            sys.exit("record the copy calibration first (--summarize-calibration)")
+        res = summarize_counters(fetch_csv, write_csv, args.steps)
+        res = {n: r for n, r in res.items() if "stream_read" not in n}  # the cache flush
+        total = sum(r["fetch_kib_median"] * 1024 * cal["fetch_scale"] + r["write_kib_median"] * 1024 * cal["write_scale"]
+                    for r in res.values())
+        family = "prefill" if "prefill" in args.workload else "decode"
+        rec.setdefault("workloads", {})[args.workload] = {
+            "kernels": res, "traffic_bytes_per_launch": total, "sources_sha256": kernel_sources_sha256(family),
+            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+                       f"--workload {args.workload} --steps {args.steps} --warmup 2 --no-cpu-baseline --no-breakdown"}
+        print(json.dumps(rec["workloads"][args.workload]))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
 
 
 def main():
@@ -406,11 +589,19 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter reference)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel durations of the last --steps dispatches of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record HBM traffic per launch of --workload in profiles/traffic.json")
+    ap.add_argument("--summarize-calibration", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record the counter scale of a --copy-calibration run in profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_counters or args.summarize_calibration:
+        return _summaries(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures a single GPU; the multi-GPU path is not implemented "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a design note "
+              "only), so only --gpus 1 runs", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -430,61 +621,73 @@ def main():
 
     import grouped_query_attention_decode_amd as gqa
     gqa.library()
+    flush = Flusher(gqa, dev)
+    small_steps, small_warmup = max(20, args.steps // 4), max(5, args.warmup // 2)
 
     def run_case(case, steps, warmup):
         log(f"[bench] {case.name}: steps={steps} warmup={warmup}")
-        r = bench_chunk(gqa, case, steps, warmup, dev)
+        if isinstance(case, W.PrefillCase):
+            r = bench_prefill(gqa, case, steps, warmup, dev, flush)
+        elif isinstance(case, (W.ChunkCase, W.PagedChunkCase)):
+            r = bench_chunk(gqa, case, steps, warmup, dev, flush)
+        else:
+            r = bench_decode(gqa, case, steps, warmup, dev, flush)
         log(f"[bench] {case.name}: {json.dumps(r)}")
-        return case, r
+        return r
 
     def run(name, steps, warmup, append=False):
         case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0)
-        tag = name + ("+append" if append else "")
-        log(f"[bench] {tag}: steps={steps} warmup={warmup}")
-        if isinstance(case, W.PrefillCase):
-            r = bench_prefill(gqa, case, steps, warmup, dev)
-        elif isinstance(case, W.ChunkCase):
-            r = bench_chunk(gqa, case, steps, warmup, dev)
-        else:
-            r = bench_decode(gqa, case, steps, warmup, dev, append)
-        log(f"[bench] {tag}: {json.dumps(r)}")
+        if not append:
+            return case, run_case(case, steps, warmup)
+        log(f"[bench] {name}+append: steps={steps} warmup={warmup}")
+        r = bench_decode(gqa, case, steps, warmup, dev, flush, append=True)
+        log(f"[bench] {name}+append: {json.dumps(r)}")
         return case, r
 
     case, head = run(args.workload, args.steps, args.warmup)
+    is_prefill = isinstance(case, (W.PrefillCase, W.ChunkCase, W.PagedChunkCase))
+    # The causal prefill is the required second entry beside a decode headline.
+    prefill_case, prefill = (None, None)
+    if args.workload != PREFILL:
+        prefill_case, prefill = run(PREFILL, args.steps, args.warmup)
     breakdown = {}
     if not args.no_breakdown:
         for name in W.WORKLOADS:
-            if name in ("toy", args.workload):
+            if name in ("toy", args.workload, PREFILL):
                 continue
-            _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
-            breakdown[name] = r
+            _, breakdown[name] = run(name, small_steps, small_warmup)
         # The decode step with the current token's cache append done by the same call.
-        for name in dict.fromkeys((args.workload, "mqa_fp8_decode_B8_L32768")):
+        for name in dict.fromkeys((args.workload, "llama7b_gqa8_decode_L2048", "mqa_fp8_decode_B8_L32768")):
             if isinstance((W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0), W.DecodeCase):
-                _, r = run(name, max(20, args.steps // 4), max(5, args.warmup // 2), append=True)
-                breakdown[name + "+append"] = r
+                _, breakdown[name + "+append"] = run(name, small_steps, small_warmup, append=True)
         # INT4 caches (4-bit fields, one scale per sequence and KV head), and prefill of a
         # 512-token chunk against a 3584-token cache.
         for name in EXTRA_WORKLOADS:
             if name != args.workload:
-                _, breakdown[name] = run(name, max(20, args.steps // 4), max(5, args.warmup // 2))
+                _, breakdown[name] = run(name, small_steps, small_warmup)
         # The chunked prefill against the same cache in shuffled pages of 16 rows.
         pcc = W.make_paged_chunk(W.chunked_prefill_512_of_4096(0), 16, seed=1)
-        _, breakdown[pcc.name] = run_case(pcc, max(20, args.steps // 4), max(5, args.warmup // 2))
+        breakdown[pcc.name] = run_case(pcc, small_steps, small_warmup)
         # The same decodes over a cache in shuffled pages of 16 rows.
         for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
             pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)
-            log(f"[bench] {pc.name}")
-            r = bench_decode(gqa, pc, max(20, args.steps // 4), max(5, args.warmup // 2), dev)
-            log(f"[bench] {pc.name}: {json.dumps(r)}")
-            breakdown[pc.name] = r
+            breakdown[pc.name] = run_case(pc, small_steps, small_warmup)
 
-    is_prefill = isinstance(case, (W.PrefillCase, W.ChunkCase))
-    achievable = None if args.no_breakdown else hbm_achievable(dev)
+    achievable = hbm_achievable(gqa, flush)
+    del flush
     cpu = None
-    if not args.no_cpu_baseline and not is_prefill:
-        log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline_decode(case)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baselines (oracle) ...")
+        if is_prefill:
+            cpu = _with_ratio(cpu_baseline_prefill(case), head["tflops"]) if isinstance(case, W.PrefillCase) else None
+        else:
+            cpu = _with_ratio(cpu_baseline_decode(case), head["kv_read_GBps"])
+        if prefill is not None:
+            prefill["cpu_baseline"] = _with_ratio(cpu_baseline_prefill(prefill_case), prefill["tflops"])
+        mqa = "mqa_fp8_decode_B8_L32768"
+        if mqa in breakdown:
+            breakdown[mqa]["cpu_baseline"] = _with_ratio(cpu_baseline_decode(W.WORKLOADS[mqa](0), budget_s=5.0),
+                                                         breakdown[mqa]["kv_read_GBps"])
         log(f"[bench] cpu baseline: {json.dumps(cpu)}")
 
     if is_prefill:
@@ -500,6 +703,7 @@ def main():
         cfg["seq_len"] = case.T
     else:
         cfg["kv_cache_len"] = case.T_cap
+        cfg["sum_seq_lens"] = int(case.seq_lens.clamp(0, case.T_cap).sum())
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
@@ -509,6 +713,7 @@ def main():
         "hbm_frac": (value / HBM_PEAK_GBS) if not is_prefill else None,
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "hbm_achievable": achievable,
         "detail": head,
         "breakdown": breakdown,

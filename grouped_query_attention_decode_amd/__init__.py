@@ -21,7 +21,7 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same runtime
 
-__all__ = ["decode", "decode_noalloc", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "status_string",
+__all__ = ["decode", "decode_noalloc", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "hbm_stream_read", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
@@ -103,6 +103,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_decode_num_splits.restype = i
     lib.gqa_decode_workspace_size.argtypes = [i] * 7
     lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.gqa_hbm_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.gqa_hbm_stream_read.restype = i
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     runtimes = _hip_runtimes_mapped()
@@ -126,6 +128,20 @@ def new_opts(**fields) -> GqaOpts:
 
 def _kv_code(kv_dtype) -> int:
     return kv_dtype if isinstance(kv_dtype, int) else DTYPES[kv_dtype]
+
+
+def hbm_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of the device tensor ``buf`` once (gqa_hbm_stream_read, a measurement
+    aid: the plain streaming-read rate, and the pass that evicts the Infinity Cache). ``sink`` is
+    a device int32 tensor of at least 1024 elements."""
+    _need_cuda(buf, "buf")
+    _need_cuda(sink, "sink", buf.device)
+    if sink.dtype != torch.int32 or sink.numel() < 1024:
+        raise ValueError("sink must be a device int32 tensor of at least 1024 elements")
+    st = library().gqa_hbm_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                       _stream_handle(stream, buf.device))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_hbm_stream_read")
 
 
 def decode_num_splits(B, H, G, D, kv_capacity, kv_dtype="bf16", num_splits=0) -> int:

@@ -28,6 +28,7 @@ SOURCES = [
     "decode_valu.hip",
     "decode_mfma.hip",
     "prefill_mfma.hip",
+    "hbm_stream.hip",
 ]
 
 ARCH = "gfx950"

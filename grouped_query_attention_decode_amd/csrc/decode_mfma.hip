@@ -137,6 +137,11 @@ __device__ __forceinline__ long row_off(const KvSrc &s, PageOffs p, int t0, int 
     }
 }
 
+// A call reads every KV row once and never again: nontemporal loads. (A plain streaming read
+// of 2 GiB on gfx950 measured 5.0-6.3 TB/s with ordinary 16-byte loads, 7.0-7.1 TB/s with
+// nontemporal ones.)
+__device__ __forceinline__ i32x4_t ld_kv(const char *p) { return __builtin_nontemporal_load((const i32x4_t *)p); }
+
 template <int KV, bool PAGED>
 __device__ __forceinline__ void load_block(Frag<KV> &f, const KvSrc &src, PageOffs pg, int t0, int ke,
                                            int lane) {
@@ -149,14 +154,14 @@ __device__ __forceinline__ void load_block(Frag<KV> &f, const KvSrc &src, PageOf
         const char *kr = src.k + row_off<PAGED, RB>(src, pg, t0, row);
         if constexpr (I4) {
             // 32 INT4 fields per lane: head dims 32*(l/16) .. +31, eight per k-step.
-            f.k[blk] = *(const i32x4_t *)(kr + 16 * (lane >> 4));
+            f.k[blk] = ld_kv(kr + 16 * (lane >> 4));
         } else if constexpr (FP8) {
             // 16 fp8 per lane: head dims 64p + 16*(l/16) .. +15 feed k-steps 2p and 2p+1.
 #pragma unroll
-            for (int p = 0; p < 2; ++p) f.k[blk * 2 + p] = *(const i32x4_t *)(kr + 64 * p + 16 * (lane >> 4));
+            for (int p = 0; p < 2; ++p) f.k[blk * 2 + p] = ld_kv(kr + 64 * p + 16 * (lane >> 4));
         } else {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.k[blk * 4 + kk] = *(const i32x4_t *)(kr + 64 * kk + 16 * (lane >> 4));
+            for (int kk = 0; kk < 4; ++kk) f.k[blk * 4 + kk] = ld_kv(kr + 64 * kk + 16 * (lane >> 4));
         }
     }
     if constexpr (I4) {
@@ -165,21 +170,21 @@ __device__ __forceinline__ void load_block(Frag<KV> &f, const KvSrc &src, PageOf
         for (int i = 0; i < 2; ++i) {
             int row = t0 + 16 * i + (lane >> 2);
             row = row < ke ? row : ke - 1;
-            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 3));
+            f.v[i] = ld_kv(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 3));
         }
     } else if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int row = t0 + 8 * i + (lane >> 3);
             row = row < ke ? row : ke - 1;
-            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 7));
+            f.v[i] = ld_kv(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 7));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             int row = t0 + 4 * i + (lane >> 4);
             row = row < ke ? row : ke - 1;
-            f.v[i] = *(const i32x4_t *)(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 15));
+            f.v[i] = ld_kv(src.v + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 15));
         }
     }
 }

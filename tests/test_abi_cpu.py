@@ -10,7 +10,7 @@ import pytest
 
 import grouped_query_attention_decode_amd as gqa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 FAKE = 0x10000  # never dereferenced: every case below is rejected on the host
 
 
@@ -20,15 +20,19 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+    """Every function that a header under include/ declares."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names.update(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"gqa_decode", "gqa_prefill", "gqa_decode_workspace_size", "gqa_status_string",
-            "gqa_opts_init", "gqa_decode_num_splits"} <= set(names)
+            "gqa_opts_init", "gqa_decode_num_splits", "gqa_decode_noalloc", "gqa_hbm_stream_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libgqa.so does not export {n}"
 
@@ -256,3 +260,11 @@ def _chunk(lib, B=2, Tq=16, H=8, G=2, D=128, scale=0.1, causal=1, ptrs=(FAKE,) *
 ])
 def test_prefill_cached_rejects(lib, kw, code):
     assert _chunk(lib, **kw) == code
+
+
+@pytest.mark.parametrize("buf,nbytes,sink", [
+    (0, 1 << 20, FAKE), (FAKE, 1 << 20, 0), (FAKE, 0, FAKE), (FAKE, 1000, FAKE), (FAKE + 8, 1 << 20, FAKE),
+])
+def test_stream_read_rejects(lib, buf, nbytes, sink):
+    """The streaming-read measurement call checks its arguments before any HIP call."""
+    assert lib.gqa_hbm_stream_read(buf, nbytes, sink, None) == INV
