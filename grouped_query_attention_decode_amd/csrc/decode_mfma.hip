@@ -54,6 +54,11 @@ __device__ __forceinline__ int tau(int blk, int m) { return ((m >> 2) << 3) + (b
 // for the transposed reads); bf16 rows have 16 chunks, fp8 rows 8.
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | (r & 8) | ((r >> 4) & 1); }
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// K tiles: the matrix-operand reads take the 16 rows tau(blk, 0..15) of a sub-block at one
+// chunk position; these XORs send them to 16 distinct 16-byte bank groups (bf16: 256-byte rows,
+// rows bits 1:0 and 4:3; fp8: 128-byte rows, two per 256 bytes, row bits 1 and 4:3).
+__device__ __forceinline__ int swzk16(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+__device__ __forceinline__ int swzk8(int r) { return ((r >> 1) & 1) | (((r >> 3) & 3) << 1); }
 
 // KV cache formats of this kernel. INT4 rows are widened to bf16 on the fly (see i4x8_to_bf16x8).
 enum : int { KV_BF16 = 0, KV_FP8 = 1, KV_I4 = 2 };
@@ -61,6 +66,13 @@ enum : int { KV_BF16 = 0, KV_FP8 = 1, KV_I4 = 2 };
 // Bytes of one cache row in HBM, and of one V-tile row in LDS (INT4 V is widened to bf16).
 template <int KV> constexpr int kRowBytes = KV == KV_FP8 ? 128 : (KV == KV_I4 ? 64 : 256);
 template <int KV> constexpr int kLdsRowBytes = KV == KV_FP8 ? 128 : 256;
+// Bytes of one K-tile row in LDS (INT4 K goes from registers straight into the operands).
+template <int KV> constexpr int kKRowBytes = KV == KV_I4 ? 0 : kRowBytes<KV>;
+// LDS of a workgroup: the V and K tiles of its four waves, later reused by the wave merge.
+template <int KV, int NHB> constexpr int kLdsBytes =
+    kWaves * kBlockT * (kLdsRowBytes<KV> + kKRowBytes<KV>) > kWaves * 16 * NHB * kDP * 4
+        ? kWaves * kBlockT * (kLdsRowBytes<KV> + kKRowBytes<KV>)
+        : kWaves * 16 * NHB * kDP * 4;
 
 // INT4 field u in a bf16 operand: bf16 bits 0x4300 | u are exactly 128 + u = 136 + code (bf16
 // has unit spacing in [128, 256)). The constant 136 is taken out of the products afterwards:
@@ -147,21 +159,32 @@ __device__ __forceinline__ void load_block(Frag<KV> &f, const KvSrc &src, PageOf
                                            int lane) {
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
+    if constexpr (I4) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        int row = t0 + tau(blk, lane & 15);
-        row = row < ke ? row : ke - 1;
-        const char *kr = src.k + row_off<PAGED, RB>(src, pg, t0, row);
-        if constexpr (I4) {
-            // 32 INT4 fields per lane: head dims 32*(l/16) .. +31, eight per k-step.
-            f.k[blk] = ld_kv(kr + 16 * (lane >> 4));
-        } else if constexpr (FP8) {
-            // 16 fp8 per lane: head dims 64p + 16*(l/16) .. +15 feed k-steps 2p and 2p+1.
+        for (int blk = 0; blk < 2; ++blk) {
+            int row = t0 + tau(blk, lane & 15);
+            row = row < ke ? row : ke - 1;
+            // 32 INT4 fields per lane: head dims 32*(l/16) .. +31, eight per k-step (a 64-byte
+            // row is one operand row: whole rows per instruction already).
+            f.k[blk] = ld_kv(src.k + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane >> 4));
+        }
+    }
+    // bf16 and fp8 K: whole rows per instruction, as V below (the matrix-operand layout would
+    // read half of every 128-byte line per instruction, which streams measurably slower); the
+    // block goes through an LDS tile and is read back in that layout.
+    if constexpr (FP8) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) f.k[blk * 2 + p] = ld_kv(kr + 64 * p + 16 * (lane >> 4));
-        } else {
+        for (int i = 0; i < 4; ++i) {
+            int row = t0 + 8 * i + (lane >> 3);
+            row = row < ke ? row : ke - 1;
+            f.k[i] = ld_kv(src.k + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 7));
+        }
+    } else if constexpr (!I4) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.k[blk * 4 + kk] = ld_kv(kr + 64 * kk + 16 * (lane >> 4));
+        for (int i = 0; i < 8; ++i) {
+            int row = t0 + 4 * i + (lane >> 4);
+            row = row < ke ? row : ke - 1;
+            f.k[i] = ld_kv(src.k + row_off<PAGED, RB>(src, pg, t0, row) + 16 * (lane & 15));
         }
     }
     if constexpr (I4) {
@@ -241,43 +264,27 @@ __device__ __forceinline__ void append_row(Frag<KV> &f, const AttnArgs &a, int b
         const int word = (int)quant_e4m3fn_x4(__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
                                               __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u), sc);
         auto gather = [&](int l0) { return i32x4_t{__shfl(word, l0), __shfl(word, l0 + 1), __shfl(word, l0 + 2), __shfl(word, l0 + 3)}; };
-        i32x4_t kc[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) kc[p] = gather((64 * p + 16 * (lane >> 4)) / 4);
-        const i32x4_t vc = gather(32 + 4 * (lane & 7));
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-                if (tau(blk, lane & 15) == rb) {
-                    f.k[blk * 2 + p] = kc[p];
-                    *(i32x4_t *)(kr + 64 * p + 16 * (lane >> 4)) = kc[p];
-                }
+        const i32x4_t kc = gather(4 * (lane & 7));       // K dims 16 (l%8) .. +15
+        const i32x4_t vc = gather(32 + 4 * (lane & 7));  // V dims likewise
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (8 * i + (lane >> 3) == rb) {
+                f.k[i] = kc;
                 f.v[i] = vc;
+                *(i32x4_t *)(kr + 16 * (lane & 7)) = kc;
                 *(i32x4_t *)(vr + 16 * (lane & 7)) = vc;
             }
     } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int d0 = 32 * kk + 8 * (lane >> 4);
-            const i32x4_t x = *(const i32x4_t *)(kn + d0);
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-                if (tau(blk, lane & 15) == rb) {
-                    f.k[blk * 4 + kk] = x;
-                    *(i32x4_t *)(kr + 2 * d0) = x;
-                }
-        }
         const int d0 = 8 * (lane & 15);
-        const i32x4_t x = *(const i32x4_t *)(vn + d0);
+        const i32x4_t xk = *(const i32x4_t *)(kn + d0);
+        const i32x4_t xv = *(const i32x4_t *)(vn + d0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (4 * i + (lane >> 4) == rb) {
-                f.v[i] = x;
-                *(i32x4_t *)(vr + 2 * d0) = x;
+                f.k[i] = xk;
+                f.v[i] = xv;
+                *(i32x4_t *)(kr + 2 * d0) = xk;
+                *(i32x4_t *)(vr + 2 * d0) = xv;
             }
     }
 }
@@ -309,6 +316,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qT[hb][kk] = i32x4_t{0, 0, 0, 0};
     char *vt = lds + wave * VT;
+    char *ktile = lds + kWaves * VT + wave * (kBlockT * kKRowBytes<KV>);
     // INT4: 136 * sum_d q[h][d] for the lane's head, to take out of every score.
     float qoff[NHB];
 #pragma unroll
@@ -391,6 +399,20 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                 *(i32x4_t *)(vt + r * RBL + 16 * ((lane & 15) ^ swz16(r))) = cur.v[i];
             }
         }
+        // K tile -> LDS likewise (bf16, fp8), for the operand-layout reads below.
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 8 * i + (lane >> 3);
+                *(i32x4_t *)(ktile + r * 128 + 16 * ((lane & 7) ^ swzk8(r))) = cur.k[i];
+            }
+        } else if constexpr (!I4) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                *(i32x4_t *)(ktile + r * 256 + 16 * ((lane & 15) ^ swzk16(r))) = cur.k[i];
+            }
+        }
         // Prefetch this slot's next block (dist rows ahead, always inside the range) before this
         // block's work; the barrier keeps the scheduler from sinking it next to its use --
         // otherwise every block waits out a full memory latency.
@@ -404,17 +426,23 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         f32x4_t s[NHB][2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
+            // Lane l: row tau(blk, l%16) of the block, head dims of k-step kk as in load_q.
             i32x4_t ka[4];
+            const int kr = tau(blk, lane & 15);
+            if constexpr (I4) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if constexpr (I4) {
-                    ka[kk] = i4x8_to_bf16x8(cur.k[blk][kk]);
-                } else if constexpr (FP8) {
-                    const i32x4_t w = cur.k[blk * 2 + (kk >> 1)];
-                    ka[kk] = e4m3x8_to_bf16x8((kk & 1) ? i32x2_t{w[2], w[3]} : i32x2_t{w[0], w[1]});
-                } else {
-                    ka[kk] = cur.k[blk * 4 + kk];
+                for (int kk = 0; kk < 4; ++kk) ka[kk] = i4x8_to_bf16x8(cur.k[blk][kk]);
+            } else if constexpr (FP8) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const i32x4_t w = *(const i32x4_t *)(ktile + kr * 128 + 16 * ((4 * p + (lane >> 4)) ^ swzk8(kr)));
+                    ka[2 * p] = e4m3x8_to_bf16x8(i32x2_t{w[0], w[1]});
+                    ka[2 * p + 1] = e4m3x8_to_bf16x8(i32x2_t{w[2], w[3]});
                 }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    ka[kk] = *(const i32x4_t *)(ktile + kr * 256 + 16 * ((4 * kk + (lane >> 4)) ^ swzk16(kr)));
             }
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) {
@@ -633,7 +661,7 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
     constexpr int RBL = kLdsRowBytes<KV>;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RBL > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RBL : kWaves * HP * kDP * 4;
+    constexpr int LDS_BYTES = kLdsBytes<KV, NHB>;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
 
@@ -700,7 +728,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
     constexpr int RBL = kLdsRowBytes<KV>;
-    constexpr int LDS_BYTES = kWaves * kBlockT * RBL > kWaves * HP * kDP * 4 ? kWaves * kBlockT * RBL : kWaves * HP * kDP * 4;
+    constexpr int LDS_BYTES = kLdsBytes<KV, NHB>;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
     __shared__ int lay_s[4];
