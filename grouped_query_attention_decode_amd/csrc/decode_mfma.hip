@@ -44,7 +44,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockT = 32;  // tokens per wave iteration
 constexpr int kD = 128;
-constexpr int kDP = kD + 4;  // row stride of the wave-merge tile: rows of 16 heads on distinct LDS banks
+constexpr int kDP = kD + 4;
+constexpr int kLenCache = 256;  // flat layout: sequence lengths kept in LDS for batches up to this  // row stride of the wave-merge tile: rows of 16 heads on distinct LDS banks
 
 // MFMA row m of token sub-block `blk` (0/1) holds token tau(blk, m) of the 32-token block,
 // so that C row 4*(l/16)+i of both sub-blocks lands in lane l as tokens 8*(l/16) + 4*blk + i.
@@ -297,14 +298,25 @@ struct PieceOut {
     bool append;  // the range ends at the sequence's last row, which the new token fills
 };
 
+// The piece a workgroup of the flat layout takes up after the current one. Its query and this
+// wave's first block of it are requested into the registers the current piece no longer needs
+// (qT, nxt) as soon as the current piece's results are out, before the workgroup leaves attend().
+struct NextPiece {
+    KvSrc src;
+    const uint16_t *q;  // its R query heads
+    int kb, ke;         // its key rows
+    bool valid;         // workgroup-uniform
+};
+
 // Attention of query heads head0 .. head0+R-1 over key rows kb .. ke-1 of one (sequence, KV
 // head), by the whole workgroup: each wave streams blocks kb + 32 (wave + 4 i), then the four
 // waves merge. The caller has requested q (qT) and this wave's first block (nxt) already.
+// With np.valid, qT and nxt are refilled with the next piece's query and first block.
 template <int NHB, int KV, bool PAGED>
 __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w)[16 * NHB], float (*l_w)[16 * NHB],
                                        int lane, int wave, long head0, int R, int bg, int kb, int ke, PieceOut po,
                                        i32x4_t (&qT)[NHB][4], Frag<KV> &nxt, const KvSrc &src, float c,
-                                       float vscale) {
+                                       float vscale, const NextPiece &np) {
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int RBL = kLdsRowBytes<KV>;  // V-tile row bytes in LDS
     constexpr int VT = kBlockT * RBL;      // V tile bytes per wave
@@ -623,10 +635,20 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             }
         }
     }
+    auto prefetch_next = [&] {
+        if (np.valid) {
+            load_q<NHB, KV>(qT, np.q, R, lane);
+            const int t0n = np.kb + wave * kBlockT;
+            if (t0n < np.ke) load_block<KV, PAGED>(nxt, np.src, fetch_pages<PAGED>(np.src, t0n), t0n, np.ke, lane);
+        }
+    };
     if (!po.direct && a.fuse_combine) {
         if (splitkv_arrive(a.counters + bg, po.n_slots))
             splitkv_merge_bf16<kThreads, kD>(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
     }
+    // (Above 32 heads per KV head the caller loads them after the return: the registers of
+    // the last-arriver merge and the next block together would spill.)
+    if constexpr (NHB <= 2) prefetch_next();
 }
 
 // The rows of (sequence b, KV head g): a slab of the contiguous cache, or the page pools and
@@ -712,8 +734,9 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     // With the in-kernel merge, a sequence whose keys all fall in this range needs no merge.
     po.direct = S == 1 || (a.fuse_combine && po.n_slots == 1);
     po.append = a.k_new && ke == L && Lraw == L;  // Lraw in 1..T_cap: the row exists
+    const NextPiece none = {};
     attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
-                            a.scale_log2 * kscale, vscale);
+                            a.scale_log2 * kscale, vscale, none);
 }
 
 // Flat layout (splitkv.h): workgroup w streams rows [w C, (w + 1) C) of the concatenated
@@ -732,6 +755,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
     __shared__ int lay_s[4];
+    // Clamped sequence lengths, read once by the layout step (batches of up to kLenCache
+    // sequences; larger ones read them from memory as they go).
+    __shared__ int len_s[kLenCache];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
@@ -753,6 +779,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
             lay_s[2] = g0 * B + b0;
             lay_s[3] = p0;
         }
+        if (B <= kLenCache)
+            for (int bb = lane; bb < B; bb += 64) len_s[bb] = clamp_len(a.seq_lens[bb], a.Tk);
     }
     __syncthreads();
     // Workgroup-uniform from here on: scalar registers, scalar branches.
@@ -776,44 +804,72 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         }
     }
 
-    int x = (int)blockIdx.x * C;
-    const int xe = x + C < N ? x + C : N;
+    const int xe = (int)blockIdx.x * C + C < N ? (int)blockIdx.x * C + C : N;
     int g = gb0 / B, b = gb0 % B;
-    while (x < xe) {
-        const int Tbraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
-        const int Tb = clamp_len(Tbraw, a.Tk);
-        const int s0 = g * Ng + Pb;  // first row of segment (b, g)
-        if (x >= s0 + Tb) {          // segment done (or empty): next one
-            Pb += Tb;
+
+    // The piece that holds row x (x < xe) of this workgroup's run: the walk over the segments
+    // moves (b, g, Pb) forward past finished and empty segments.
+    struct Piece {
+        int b, g, kb, ke, Tb, Tbraw, s0, Pb;
+    };
+    auto piece_at = [&](int x) {
+        for (;;) {
+            const int Tbraw = __builtin_amdgcn_readfirstlane(B <= kLenCache ? len_s[b] : a.seq_lens[b]);
+            const int Tb = clamp_len(Tbraw, a.Tk);
+            const int s0 = g * Ng + Pb;  // first row of segment (b, g)
+            if (x < s0 + Tb) return Piece{b, g, x - s0, xe - s0 < Tb ? xe - s0 : Tb, Tb, Tbraw, s0, Pb};
+            Pb += Tb;  // segment done (or empty): next one
             if (++b == B) {
                 b = 0;
                 Pb = 0;
                 ++g;
             }
-            continue;
         }
-        const int kb = x - s0;
-        const int ke = xe - s0 < Tb ? xe - s0 : Tb;
-        const int bg = b * G + g;
-        const long head0 = (long)b * H + (long)g * R;
-        PieceOut po;
-        po.n_slots = flat_pieces(Ng, C, Pb, Tb, g);
-        po.slot = (int)blockIdx.x - (int)((unsigned)s0 / (unsigned)C);
-        po.direct = po.n_slots == 1;
-        po.append = a.k_new && ke == Tb && Tbraw == Tb;
+    };
 
-        i32x4_t qT[NHB][4];
-        load_q<NHB, KV>(qT, static_cast<const uint16_t *>(a.q) + head0 * kD, R, lane);
+    if ((int)blockIdx.x * C >= xe) return;
+    Piece cur = piece_at((int)blockIdx.x * C);
+    i32x4_t qT[NHB][4];
+    Frag<KV> nxt;
+    {
+        load_q<NHB, KV>(qT, static_cast<const uint16_t *>(a.q) + ((long)cur.b * H + (long)cur.g * R) * kD, R, lane);
+        const KvSrc src = kv_src<PAGED, RB>(a, cur.b, cur.g, cur.b * G + cur.g);
+        const int t0 = cur.kb + wave * kBlockT;
+        if (t0 < cur.ke) load_block<KV, PAGED>(nxt, src, fetch_pages<PAGED>(src, t0), t0, cur.ke, lane);
+    }
+    for (;;) {
+        const int bg = cur.b * G + cur.g;
+        const long head0 = (long)cur.b * H + (long)cur.g * R;
+        PieceOut po;
+        po.n_slots = flat_pieces(Ng, C, cur.Pb, cur.Tb, cur.g);
+        po.slot = (int)blockIdx.x - (int)((unsigned)cur.s0 / (unsigned)C);
+        po.direct = po.n_slots == 1;
+        // The length as stored (not clamped) decides whether row L-1 exists for an append.
+        po.append = a.k_new && cur.ke == cur.Tb && __builtin_amdgcn_readfirstlane(a.seq_lens[cur.b]) == cur.Tb;
         const float kscale = FP8 || I4 ? a.k_scale[bg] : 1.f;
         const float vscale = FP8 || I4 ? a.v_scale[bg] : 1.f;
-        const KvSrc src = kv_src<PAGED, RB>(a, b, g, bg);
-        Frag<KV> nxt;
-        if (kb + wave * kBlockT < ke)
-            load_block<KV, PAGED>(nxt, src, fetch_pages<PAGED>(src, kb + wave * kBlockT), kb + wave * kBlockT, ke, lane);
-        attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
-                         a.scale_log2 * kscale, vscale);
+        const KvSrc src = kv_src<PAGED, RB>(a, cur.b, cur.g, bg);
+        // The piece after this one, if the run goes on.
+        NextPiece np = {};
+        Piece following = cur;
+        np.valid = cur.s0 + cur.ke < xe;
+        if (np.valid) {
+            following = piece_at(cur.s0 + cur.ke);
+            np.src = kv_src<PAGED, RB>(a, following.b, following.g, following.b * G + following.g);
+            np.q = static_cast<const uint16_t *>(a.q) + ((long)following.b * H + (long)following.g * R) * kD;
+            np.kb = following.kb;
+            np.ke = following.ke;
+        }
+        attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, cur.kb, cur.ke, po, qT, nxt, src,
+                               a.scale_log2 * kscale, vscale, np);
+        if (!np.valid) break;
+        if constexpr (NHB > 2) {
+            load_q<NHB, KV>(qT, np.q, R, lane);
+            const int t0 = np.kb + wave * kBlockT;
+            if (t0 < np.ke) load_block<KV, PAGED>(nxt, np.src, fetch_pages<PAGED>(np.src, t0), t0, np.ke, lane);
+        }
         __syncthreads();  // the next piece reuses the LDS tiles
-        x = s0 + ke;
+        cur = following;
     }
 }
 

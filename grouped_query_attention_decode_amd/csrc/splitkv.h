@@ -84,13 +84,19 @@ __device__ __forceinline__ f32x4_t splitkv_load4(__amdgpu_buffer_rsrc_t r, unsig
 }
 
 // All threads call this after writing their partials with splitkv_store(.., 1). Returns, in
-// every thread of the workgroup, whether this workgroup arrived last for its group.
-__device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active) {
+// every thread of the workgroup, whether this workgroup arrived last for its group. `then` runs
+// in every thread once the partial stores have completed, after the counter increment has been
+// issued and before its result is awaited: loads it issues (the next piece's first block) are
+// in flight during that round trip instead of after it.
+template <typename Then>
+__device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active, Then then) {
     __shared__ int last_s;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
     __syncthreads();
+    int old = 0;
+    if (threadIdx.x == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    then();
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = old == n_active - 1;
         // Every other range has arrived: reset for the next call.
         if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -98,6 +104,10 @@ __device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active) {
     }
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(last_s) != 0;
+}
+
+__device__ __forceinline__ bool splitkv_arrive(int *counter, int n_active) {
+    return splitkv_arrive(counter, n_active, [] {});
 }
 
 // Largest R * n_active a fused merge handles (the host checks R * S against it).
