@@ -765,13 +765,13 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
 
     // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row.
     if (wave == 0) {
-        const int Ng = flat_total(a.seq_lens, B, a.Tk, lane);
+        const int Ng = flat_total(a.seq_lens, B, a.Tk, a.flat_pad, lane);
         const int C = flat_chunk(G * Ng, gridDim.x, a.flat_cmin);
         const int x0 = (int)blockIdx.x * C;
         int b0 = 0, p0 = 0, g0 = 0;
         if (x0 < G * Ng) {
             g0 = x0 / Ng;
-            flat_find(a.seq_lens, B, a.Tk, x0 - g0 * Ng, lane, b0, p0);
+            flat_find(a.seq_lens, B, a.Tk, a.flat_pad, x0 - g0 * Ng, lane, b0, p0);
         }
         if (lane == 0) {
             lay_s[0] = Ng;
@@ -808,17 +808,23 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     int g = gb0 / B, b = gb0 % B;
 
     // The piece that holds row x (x < xe) of this workgroup's run: the walk over the segments
-    // moves (b, g, Pb) forward past finished and empty segments.
+    // moves (b, g, Pb) forward past finished and empty segments. r0 is the segment's first valid
+    // row; the piece covers its valid rows kb .. ke-1, none when the run ends in the segment's
+    // pad rows (ke <= kb).
     struct Piece {
-        int b, g, kb, ke, Tb, Tbraw, s0, Pb;
+        int b, g, kb, ke, Tb, r0, Pb;
     };
+    const int pad = a.flat_pad;
     auto piece_at = [&](int x) {
         for (;;) {
-            const int Tbraw = __builtin_amdgcn_readfirstlane(B <= kLenCache ? len_s[b] : a.seq_lens[b]);
-            const int Tb = clamp_len(Tbraw, a.Tk);
-            const int s0 = g * Ng + Pb;  // first row of segment (b, g)
-            if (x < s0 + Tb) return Piece{b, g, x - s0, xe - s0 < Tb ? xe - s0 : Tb, Tb, Tbraw, s0, Pb};
-            Pb += Tb;  // segment done (or empty): next one
+            const int Tb = clamp_len(__builtin_amdgcn_readfirstlane(B <= kLenCache ? len_s[b] : a.seq_lens[b]), a.Tk);
+            const int s0 = g * Ng + Pb;  // first row of segment (b, g), pad rows included
+            const int X = flat_span(Tb, pad);
+            if (x < s0 + X) {
+                const int r0 = s0 + pad;
+                return Piece{b, g, x > r0 ? x - r0 : 0, (xe < s0 + X ? xe : s0 + X) - r0, Tb, r0, Pb};
+            }
+            Pb += X;  // segment done (or empty): next one
             if (++b == B) {
                 b = 0;
                 Pb = 0;
@@ -829,6 +835,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
 
     if ((int)blockIdx.x * C >= xe) return;
     Piece cur = piece_at((int)blockIdx.x * C);
+    if (cur.ke <= cur.kb) return;  // the run holds pad rows only
     i32x4_t qT[NHB][4];
     Frag<KV> nxt;
     {
@@ -841,8 +848,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         const int bg = cur.b * G + cur.g;
         const long head0 = (long)cur.b * H + (long)cur.g * R;
         PieceOut po;
-        po.n_slots = flat_pieces(Ng, C, cur.Pb, cur.Tb, cur.g);
-        po.slot = (int)blockIdx.x - (int)((unsigned)cur.s0 / (unsigned)C);
+        po.n_slots = flat_pieces(Ng, C, cur.Pb, cur.Tb, cur.g, pad);
+        po.slot = (int)blockIdx.x - (int)((unsigned)cur.r0 / (unsigned)C);
         po.direct = po.n_slots == 1;
         // The length as stored (not clamped) decides whether row L-1 exists for an append.
         po.append = a.k_new && cur.ke == cur.Tb && __builtin_amdgcn_readfirstlane(a.seq_lens[cur.b]) == cur.Tb;
@@ -852,9 +859,12 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         // The piece after this one, if the run goes on.
         NextPiece np = {};
         Piece following = cur;
-        np.valid = cur.s0 + cur.ke < xe;
+        np.valid = cur.r0 + cur.ke < xe;
         if (np.valid) {
-            following = piece_at(cur.s0 + cur.ke);
+            following = piece_at(cur.r0 + cur.ke);
+            np.valid = following.ke > following.kb;
+        }
+        if (np.valid) {
             np.src = kv_src<PAGED, RB>(a, following.b, following.g, following.b * G + following.g);
             np.q = static_cast<const uint16_t *>(a.q) + ((long)following.b * H + (long)following.g * R) * kD;
             np.kb = following.kb;

@@ -95,14 +95,26 @@ struct DecodePlan {
     int split_len = 0;  // uniform
     int nw = 0;         // flat: workgroups
     int cmin = 0;       // flat: fewest rows per workgroup
+    int pad = 0;        // flat: rows of no work in front of each non-empty segment
     int fuse = 0;       // merge inside the decode kernel
 };
 
 constexpr int kNominalCUs = 256;
 constexpr int kFlatMinBatch = 16;
 
-bool flat_possible(int B, int G, int T_cap, int path, int requested) {
-    return path == GQA_PATH_MFMA && requested == 0 && (long)B * G * T_cap < (1L << 31);
+// The fixed cost of one piece of the flat layout (its first round trip, the merge of its waves,
+// its partials and arrival: a few microseconds at the ~27 GB/s one CU streams) as the K/V bytes
+// a workgroup would stream meanwhile, and as rows of a cache type. Measured on the ragged
+// Llama-70B batch (pads of 0 / 40 / 80 / 120 / 160 / 240 KiB): bf16 35.4 / 34.9 / 34.6 / 33.7 /
+// 33.8 / 34.0 us; its INT4 cache 20.9 / 20.1 / 19.7 / 20.0 / 20.6 / 22.5 us; a ragged fp8 MQA
+// batch (B16 H32 G1, 2k-16k keys) 26.0 / 23.9 / 22.2 / 21.5 / 21.5 / 21.3 us.
+int flat_pad_rows(long D, int kv_dtype) {
+    const long cost = kv_dtype == DT_INT4 ? 80 * 1024 : 120 * 1024;
+    return (int)(cost / (2 * row_bytes(kv_dtype, D)));
+}
+
+bool flat_possible(int B, int G, int T_cap, int D, int kv_dtype, int path, int requested) {
+    return path == GQA_PATH_MFMA && requested == 0 && (long)B * G * (T_cap + flat_pad_rows(D, kv_dtype)) < (1L << 31);
 }
 
 // `path` is the resolved kernel family (not AUTO); `layout` a gqa_layout the caller checked.
@@ -110,10 +122,11 @@ DecodePlan plan_decode(int B, int H, int G, int D, int T_cap, int kv_dtype, int 
     DecodePlan p;
     const long R = H / G;
     const bool mfma_path = path == GQA_PATH_MFMA;
-    const bool flat = flat_possible(B, G, T_cap, path, requested) &&
+    const bool flat = flat_possible(B, G, T_cap, D, kv_dtype, path, requested) &&
                       (layout == GQA_LAYOUT_FLAT || (layout == GQA_LAYOUT_AUTO && B >= kFlatMinBatch));
     if (flat) {
         p.flat = 1;
+        p.pad = flat_pad_rows(D, kv_dtype);
         // One workgroup per CU: each streams a long run of rows, so the per-piece fixed costs
         // (lengths, first block, merge) stay small against it.
         p.nw = kNominalCUs;
@@ -339,7 +352,7 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     if (path == GQA_PATH_VALU && !decode_valu_supports(a)) return GQA_ERR_UNSUPPORTED;
     if (path == GQA_PATH_MFMA && !decode_mfma_supports(a)) return GQA_ERR_UNSUPPORTED;
 
-    if (o.layout == GQA_LAYOUT_FLAT && !flat_possible(B, G, o.kv_capacity, path, o.num_splits))
+    if (o.layout == GQA_LAYOUT_FLAT && !flat_possible(B, G, o.kv_capacity, D, o.kv_dtype, path, o.num_splits))
         return GQA_ERR_UNSUPPORTED;
     const DecodePlan plan = plan_decode(B, H, G, D, o.kv_capacity, o.kv_dtype, o.num_splits, path, o.layout);
     a.num_splits = plan.S;
@@ -347,6 +360,7 @@ gqa_status decode_impl(const void *q, const void *k_cache, const void *v_cache, 
     a.flat = plan.flat;
     a.flat_nw = plan.nw;
     a.flat_cmin = plan.cmin;
+    a.flat_pad = plan.pad;
 
     const size_t need = workspace_bytes_for(B, H, G, D, a.num_splits);
     if (need > 0 && o.workspace && o.workspace_bytes < need) return GQA_ERR_WORKSPACE;

@@ -40,6 +40,7 @@ struct AttnArgs {
     int flat;                 // decode: 1 = flat layout of a ragged batch (splitkv.h)
     int flat_nw;              // flat layout: workgroups of the decode kernel
     int flat_cmin;            // flat layout: fewest rows per workgroup
+    int flat_pad;             // flat layout: rows of no work in front of each non-empty segment
     float scale_log2;         // scale * log2(e): scores are kept in the base-2 domain
     int q_dtype, kv_dtype;
 };

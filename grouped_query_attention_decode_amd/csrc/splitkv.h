@@ -207,15 +207,22 @@ __device__ __forceinline__ void splitkv_merge_bf16(const AttnArgs &a, long head0
 
 // ---- Flat layout of a ragged batch ----
 // The valid rows of every (sequence b, KV head g) segment are laid end to end, KV head
-// outermost: segment (b, g) starts at g * Ng + P_b, with T_b the clamped length of sequence
-// b, Ng = sum_b T_b and P_b = sum_{b' < b} T_b'. Workgroup w takes rows [w C, (w + 1) C) of
-// this sequence, so every workgroup streams the same number of rows whatever the lengths.
-// The part of a segment that one workgroup covers is a "piece"; the pieces of segment (b, g)
-// belong to workgroups first .. last = (start) / C .. (start + T_b - 1) / C and leave their
-// partials in slots 0 .. last - first. The host uses this layout only when B * G * T_cap
-// < 2^31, so every row index fits in 32 bits.
+// outermost, each non-empty segment preceded by `pad` rows of no work: segment (b, g) spans
+// X_b = T_b + pad rows (0 when T_b = 0) from g * Ng + P_b, its valid rows from g * Ng + P_b +
+// pad, with T_b the clamped length of sequence b, Ng = sum_b X_b and P_b = sum_{b' < b} X_b'.
+// Workgroup w takes rows [w C, (w + 1) C) of this sequence. The part of a segment's valid rows
+// that one workgroup covers is a "piece"; each piece has a fixed cost (its first round trip,
+// the merge of its waves, its partials and arrival), which the pad rows stand for: a
+// workgroup whose run is cut into several pieces gets correspondingly fewer valid rows, so
+// every workgroup has about the same work whatever the lengths. The pieces of segment (b, g)
+// belong to workgroups first .. last = r0 / C .. (r0 + T_b - 1) / C, r0 being its first valid
+// row, and leave their partials in slots 0 .. last - first. The host uses this layout only when
+// B * G * (T_cap + pad) < 2^31, so every row index fits in 32 bits.
 
 __device__ __forceinline__ int clamp_len(int L, int Tk) { return L < 0 ? 0 : (L > Tk ? Tk : L); }
+
+// Rows that a sequence of T valid rows occupies in each KV head's run.
+__device__ __forceinline__ int flat_span(int T, int pad) { return T > 0 ? T + pad : 0; }
 
 // Rows per workgroup: the N rows spread over nw workgroups, at least cmin, a multiple of 32.
 __device__ __forceinline__ int flat_chunk(int N, int nw, int cmin) {
@@ -247,26 +254,26 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
     return x;
 }
 
-// Whole wave: Ng = sum_b T_b.
-__device__ __forceinline__ int flat_total(const int32_t *seq_lens, int B, int Tk, int lane) {
+// Whole wave: Ng = sum_b X_b.
+__device__ __forceinline__ int flat_total(const int32_t *seq_lens, int B, int Tk, int pad, int lane) {
     int tot = 0;
     for (int k0 = 0; k0 < B; k0 += 64) {
         const int b = k0 + lane;
-        tot += wave_sum(b < B ? clamp_len(seq_lens[b], Tk) : 0);
+        tot += wave_sum(b < B ? flat_span(clamp_len(seq_lens[b], Tk), pad) : 0);
     }
     return tot;
 }
 
 // Whole wave: the sequence b holding row `local` (0 <= local < Ng) of a KV head's run of
 // segments, and its start P_b.
-__device__ __forceinline__ void flat_find(const int32_t *seq_lens, int B, int Tk, int local, int lane, int &b_out,
-                                          int &p_out) {
+__device__ __forceinline__ void flat_find(const int32_t *seq_lens, int B, int Tk, int pad, int local, int lane,
+                                          int &b_out, int &p_out) {
     int run = 0;
     b_out = B - 1;
     p_out = 0;
     for (int k0 = 0; k0 < B; k0 += 64) {
         const int b = k0 + lane;
-        const int t = b < B ? clamp_len(seq_lens[b], Tk) : 0;
+        const int t = b < B ? flat_span(clamp_len(seq_lens[b], Tk), pad) : 0;
         const int incl = wave_scan(t, lane) + run;
         const int excl = incl - t;
         const unsigned long long hit = __ballot(b < B && excl <= local && local < incl);
@@ -281,10 +288,10 @@ __device__ __forceinline__ void flat_find(const int32_t *seq_lens, int B, int Tk
 }
 
 // Number of pieces (partial slots) of segment (b, g): 0 for an empty sequence.
-__device__ __forceinline__ int flat_pieces(int Ng, int C, int Pb, int Tb, int g) {
+__device__ __forceinline__ int flat_pieces(int Ng, int C, int Pb, int Tb, int g, int pad) {
     if (Tb <= 0) return 0;
-    const unsigned s0 = (unsigned)(g * Ng + Pb);
-    return (int)((s0 + Tb - 1) / (unsigned)C - s0 / (unsigned)C + 1);
+    const unsigned r0 = (unsigned)(g * Ng + Pb + pad);  // its first valid row
+    return (int)((r0 + Tb - 1) / (unsigned)C - r0 / (unsigned)C + 1);
 }
 
 }  // namespace gqa

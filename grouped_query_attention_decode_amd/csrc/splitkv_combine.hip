@@ -28,7 +28,7 @@ __device__ int flat_row_pieces(const AttnArgs &a, int b, int g) {
     __shared__ int red_s[2][4];
     int tot = 0, pre = 0;
     for (int bb = threadIdx.x; bb < a.B; bb += blockDim.x) {
-        const int t = clamp_len(a.seq_lens[bb], a.Tk);
+        const int t = flat_span(clamp_len(a.seq_lens[bb], a.Tk), a.flat_pad);
         tot += t;
         if (bb < b) pre += t;
     }
@@ -48,7 +48,7 @@ __device__ int flat_row_pieces(const AttnArgs &a, int b, int g) {
     Ng = __builtin_amdgcn_readfirstlane(Ng);
     Pb = __builtin_amdgcn_readfirstlane(Pb);
     const int C = flat_chunk(a.G * Ng, a.flat_nw, a.flat_cmin);
-    return flat_pieces(Ng, C, Pb, clamp_len(a.seq_lens[b], a.Tk), g);
+    return flat_pieces(Ng, C, Pb, clamp_len(a.seq_lens[b], a.Tk), g, a.flat_pad);
 }
 
 // One workgroup per (sequence, query head); thread d owns head dim d. Uniform layout: all

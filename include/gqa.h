@@ -83,7 +83,7 @@ typedef enum gqa_path {
 /* Decode work layout. UNIFORM cuts every (sequence, KV head) into the same number of key
  * ranges (num_splits); FLAT lays the valid keys of all sequences end to end and gives every
  * workgroup the same number of them, so a batch of very unequal lengths still keeps every
- * compute unit busy (matrix-core family only, batches with B * G * kv_capacity < 2^31).
+ * compute unit busy (matrix-core family only, batches with B * G * (kv_capacity + 1024) < 2^31).
  * AUTO takes FLAT for batches of 16 or more sequences on the matrix-core family and UNIFORM
  * otherwise. The split-KV scheme these build on is the one of ["GQA revolution ...", section
  * on split-KV block computation]; the flat layout is this library's own. */
