@@ -763,15 +763,29 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
     const int G = a.G, H = a.H, R = H / G, B = a.B;
 
-    // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row.
+    // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row. The
+    // lengths are read from memory once (into LDS, for batches up to kLenCache; the search for
+    // the first segment then runs on them there), which is the only round trip before this
+    // workgroup's first K/V requests.
     if (wave == 0) {
-        const int Ng = flat_total(a.seq_lens, B, a.Tk, a.flat_pad, lane);
+        const bool cached = B <= kLenCache;
+        int Ng = 0;
+        for (int k0 = 0; k0 < B; k0 += 64) {
+            const int bb = k0 + lane;
+            const int t = bb < B ? clamp_len(a.seq_lens[bb], a.Tk) : 0;
+            if (cached && bb < B) len_s[bb] = t;
+            Ng += wave_sum(flat_span(t, a.flat_pad));
+        }
         const int C = flat_chunk(G * Ng, gridDim.x, a.flat_cmin);
         const int x0 = (int)blockIdx.x * C;
         int b0 = 0, p0 = 0, g0 = 0;
         if (x0 < G * Ng) {
             g0 = x0 / Ng;
-            flat_find(a.seq_lens, B, a.Tk, a.flat_pad, x0 - g0 * Ng, lane, b0, p0);
+            if (cached)
+                flat_find([&](int bb) { return len_s[bb]; }, B, a.flat_pad, x0 - g0 * Ng, lane, b0, p0);
+            else
+                flat_find([&](int bb) { return clamp_len(a.seq_lens[bb], a.Tk); }, B, a.flat_pad, x0 - g0 * Ng, lane,
+                          b0, p0);
         }
         if (lane == 0) {
             lay_s[0] = Ng;
@@ -779,8 +793,6 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
             lay_s[2] = g0 * B + b0;
             lay_s[3] = p0;
         }
-        if (B <= kLenCache)
-            for (int bb = lane; bb < B; bb += 64) len_s[bb] = clamp_len(a.seq_lens[bb], a.Tk);
     }
     __syncthreads();
     // Workgroup-uniform from here on: scalar registers, scalar branches.

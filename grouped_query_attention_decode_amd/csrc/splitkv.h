@@ -254,26 +254,16 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
     return x;
 }
 
-// Whole wave: Ng = sum_b X_b.
-__device__ __forceinline__ int flat_total(const int32_t *seq_lens, int B, int Tk, int pad, int lane) {
-    int tot = 0;
-    for (int k0 = 0; k0 < B; k0 += 64) {
-        const int b = k0 + lane;
-        tot += wave_sum(b < B ? flat_span(clamp_len(seq_lens[b], Tk), pad) : 0);
-    }
-    return tot;
-}
-
 // Whole wave: the sequence b holding row `local` (0 <= local < Ng) of a KV head's run of
-// segments, and its start P_b.
-__device__ __forceinline__ void flat_find(const int32_t *seq_lens, int B, int Tk, int pad, int local, int lane,
-                                          int &b_out, int &p_out) {
+// segments, and its start P_b. len(b) gives the clamped length of sequence b.
+template <typename Len>
+__device__ __forceinline__ void flat_find(Len len, int B, int pad, int local, int lane, int &b_out, int &p_out) {
     int run = 0;
     b_out = B - 1;
     p_out = 0;
     for (int k0 = 0; k0 < B; k0 += 64) {
         const int b = k0 + lane;
-        const int t = b < B ? flat_span(clamp_len(seq_lens[b], Tk), pad) : 0;
+        const int t = b < B ? flat_span(len(b), pad) : 0;
         const int incl = wave_scan(t, lane) + run;
         const int excl = incl - t;
         const unsigned long long hit = __ballot(b < B && excl <= local && local < incl);
