@@ -82,6 +82,15 @@ EXTRA_WORKLOADS = {
     "gqa8_chunked_prefill_B4_Tq512_L4096_fp8": W.chunked_prefill_512_of_4096_fp8,
 }
 
+# Narrow-group decodes (R = 2, 4, 8 query heads per KV head) for the comparison of the
+# vector-ALU and matrix-core kernel families (--workload with --path); not in the breakdown.
+NARROW_WORKLOADS = {
+    "gqa_decode_B1_H16_G8_L2048": lambda seed: W.narrow_group_decode(16, seed),
+    "gqa_decode_B1_H32_G8_L2048": lambda seed: W.narrow_group_decode(32, seed),
+    "gqa_decode_B1_H64_G8_L2048": lambda seed: W.narrow_group_decode(64, seed),
+}
+
+
 def kernel_sources_sha256(family: str) -> str:
     """Hash of the sources of one kernel family; counters taken on other sources do not apply."""
     import hashlib
@@ -149,7 +158,7 @@ def prefill_bytes(c: W.PrefillCase) -> int:
 
 # ------------------------------------------------------------------------------------
 
-def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
+def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False, path="auto"):
     paged = isinstance(c, W.PagedDecodeCase)
     kk, vv = (c.k_pages, c.v_pages) if paged else (c.k_cache, c.v_cache)
     kv_alloc = 2 * kk.numel() * kk.element_size()
@@ -179,9 +188,9 @@ def make_decode_runner(gqa, c: W.DecodeCase, dev, append=False):
         state["i"] += 1
         if paged:
             gqa.decode_paged(q, k, v, table, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws,
-                             **new)
+                             path=path, **new)
         else:
-            gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, **new)
+            gqa.decode(q, k, v, lens, out=out, scale=c.scale, k_scale=ks, v_scale=vs, workspace=ws, path=path, **new)
 
     return step, nrep, out
 
@@ -333,8 +342,8 @@ def time_steps(step, steps, warmup, flush, graph=True):
     return res
 
 
-def bench_decode(gqa, c, steps, warmup, dev, flush, append=False):
-    step, nrep, _ = make_decode_runner(gqa, c, dev, append)
+def bench_decode(gqa, c, steps, warmup, dev, flush, append=False, path="auto"):
+    step, nrep, _ = make_decode_runner(gqa, c, dev, append, path)
     t = time_steps(step, steps, warmup, flush)
     by = decode_bytes(c, append)
     s = t["ms_per_step"] * 1e-3
@@ -342,7 +351,7 @@ def bench_decode(gqa, c, steps, warmup, dev, flush, append=False):
     achieved = by["total"] / launch / 1e9
     return {
         "workload": c.name, "B": c.B, "H": c.H, "G": c.G, "D": c.D, "T_cap": c.T_cap,
-        "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype, "cache_append": append,
+        "sum_seq_lens": int(c.seq_lens.sum()), "kv_dtype": c.kv_dtype, "cache_append": append, "path": path,
         "page_size": c.page_size if isinstance(c, W.PagedDecodeCase) else None,
         "splits": gqa.decode_num_splits(c.B, c.H, c.G, c.D, c.T_cap, c.kv_dtype),
         "kv_bytes": by["kv"], "algorithmic_bytes": by["total"], "flops": decode_flops(c),
@@ -521,6 +530,26 @@ def _counter_per_dispatch(path, counter):
     return by
 
 
+def summarize_pmc(path, steps):
+    """Median of every counter per kernel over its last `steps` dispatches of a rocprofv3
+    --pmc CSV: {kernel: {counter: value}}."""
+    rows = _read_csv(path)
+    per = {}
+    for r in rows:
+        key = (_kernel_name(r), r["Counter_Name"], int(r.get("Dispatch_Id") or r.get("Correlation_Id")))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (name, ctr, did), v in sorted(per.items(), key=lambda kv: kv[0][2]):
+        by.setdefault(name, {}).setdefault(ctr, []).append(v)
+    out = {}
+    for name, ctrs in by.items():
+        out[name] = {}
+        for ctr, vals in ctrs.items():
+            last = sorted(vals[-steps:])
+            out[name][ctr] = last[len(last) // 2]
+    return out
+
+
 def summarize_counters(fetch_csv, write_csv, steps):
     """Median FETCH_SIZE / WRITE_SIZE (KiB) per kernel over its last `steps` dispatches."""
     f, w = _counter_per_dispatch(fetch_csv, "FETCH_SIZE"), _counter_per_dispatch(write_csv, "WRITE_SIZE")
@@ -534,6 +563,13 @@ def summarize_counters(fetch_csv, write_csv, steps):
 def _summaries(args):
     """The --summarize-* modes: read rocprofv3 CSV output, print (and for counters record) the
     figures kept under profiles/. No GPU needed."""
+    if args.summarize_pmc:
+        res = summarize_pmc(args.summarize_pmc, args.steps)
+        ctrs = sorted({c for r in res.values() for c in r})
+        print(f"{'kernel':58s} " + " ".join(f"{c:>16s}" for c in ctrs))
+        for name, r in res.items():
+            print(f"{name[:58]:58s} " + " ".join(f"{r.get(c, float('nan')):16.4g}" for c in ctrs))
+        return
     if args.summarize_trace:
         res = summarize_trace(args.summarize_trace, args.steps)
         print(f"{'kernel':58s} {'disp':>5s} {'timed':>5s} {'median_us':>10s} {'mean_us':>9s} {'min_us':>8s} {'max_us':>8s}")
@@ -584,19 +620,23 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE,
-                    choices=[k for k in W.WORKLOADS if k != "toy"] + list(EXTRA_WORKLOADS))
+                    choices=[k for k in W.WORKLOADS if k != "toy"] + list(EXTRA_WORKLOADS) + list(NARROW_WORKLOADS))
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "generic"],
+                    help="decode kernel family for --workload (the breakdown always runs auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter reference)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel durations of the last --steps dispatches of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
+                    help="per-kernel medians of every counter of a rocprofv3 --pmc run (last --steps dispatches)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="record HBM traffic per launch of --workload in profiles/traffic.json")
     ap.add_argument("--summarize-calibration", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="record the counter scale of a --copy-calibration run in profiles/traffic.json")
     args = ap.parse_args()
-    if args.summarize_trace or args.summarize_counters or args.summarize_calibration:
+    if args.summarize_trace or args.summarize_counters or args.summarize_calibration or args.summarize_pmc:
         return _summaries(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -635,8 +675,13 @@ def main():
         log(f"[bench] {case.name}: {json.dumps(r)}")
         return r
 
-    def run(name, steps, warmup, append=False):
-        case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0)
+    def run(name, steps, warmup, append=False, path="auto"):
+        case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS.get(name) or NARROW_WORKLOADS[name])(0)
+        if path != "auto" and isinstance(case, W.DecodeCase):
+            log(f"[bench] {name} path={path}: steps={steps} warmup={warmup}")
+            r = bench_decode(gqa, case, steps, warmup, dev, flush, path=path)
+            log(f"[bench] {name} path={path}: {json.dumps(r)}")
+            return case, r
         if not append:
             return case, run_case(case, steps, warmup)
         log(f"[bench] {name}+append: steps={steps} warmup={warmup}")
@@ -644,11 +689,11 @@ def main():
         log(f"[bench] {name}+append: {json.dumps(r)}")
         return case, r
 
-    case, head = run(args.workload, args.steps, args.warmup)
+    case, head = run(args.workload, args.steps, args.warmup, path=args.path)
     is_prefill = isinstance(case, (W.PrefillCase, W.ChunkCase, W.PagedChunkCase))
     # The causal prefill is the required second entry beside a decode headline.
     prefill_case, prefill = (None, None)
-    if args.workload != PREFILL:
+    if args.workload != PREFILL and not args.no_breakdown:
         prefill_case, prefill = run(PREFILL, args.steps, args.warmup)
     breakdown = {}
     if not args.no_breakdown:
@@ -658,7 +703,8 @@ def main():
             _, breakdown[name] = run(name, small_steps, small_warmup)
         # The decode step with the current token's cache append done by the same call.
         for name in dict.fromkeys((args.workload, "llama7b_gqa8_decode_L2048", "mqa_fp8_decode_B8_L32768")):
-            if isinstance((W.WORKLOADS.get(name) or EXTRA_WORKLOADS[name])(0), W.DecodeCase):
+            if isinstance((W.WORKLOADS.get(name) or EXTRA_WORKLOADS.get(name) or NARROW_WORKLOADS[name])(0),
+                          W.DecodeCase):
                 _, breakdown[name + "+append"] = run(name, small_steps, small_warmup, append=True)
         # INT4 caches (4-bit fields, one scale per sequence and KV head), and prefill of a
         # 512-token chunk against a 3584-token cache.

@@ -469,6 +469,13 @@ def chunked_prefill_512_of_4096_fp8(seed=0) -> ChunkCase:
                       kv_dtype=FP8)
 
 
+def narrow_group_decode(H: int, seed=0) -> DecodeCase:
+    """The Llama-2-7B-shaped decode with H query heads over its 8 KV heads (R = H / 8 query heads
+    per KV head): B1 D128, 2048 cached tokens, bf16. For the comparison of the vector-ALU and
+    matrix-core decode kernels at narrow groups (R = 2, 4, 8)."""
+    return make_decode(1, H, 8, 128, 2048, T_cap=2048, seed=seed, name=f"gqa_decode_B1_H{H}_G8_L2048")
+
+
 WORKLOADS = {
     "toy": None,  # prefill + two decode steps; see toy_prefill / toy_decode_steps
     "llama7b_gqa8_decode_L2048": llama7b_gqa8_decode,
