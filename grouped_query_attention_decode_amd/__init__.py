@@ -24,7 +24,10 @@ import torch  # loads torch's HIP runtime first, so libgqa.so binds to that same
 __all__ = ["decode", "decode_noalloc", "decode_paged", "prefill", "prefill_cached", "prefill_paged", "decode_num_splits", "decode_workspace_size", "hbm_stream_read", "status_string",
            "GqaError", "library", "LIBRARY_PATH", "GqaOpts", "PATHS", "DTYPES", "LAYOUTS"]
 
-LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+# The library built in this package; GQA_LIBRARY_PATH may name another build of the same sources
+# (the host-sanitized one for the CPU tests of the C ABI).
+LIBRARY_PATH = os.environ.get("GQA_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                                  "libgqa.so")
 
 GQA_OK = 0
 DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3fn": 2, "int4": 3}

@@ -40,8 +40,17 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+# Host code only (the C ABI layer and launch code) under AddressSanitizer and
+# UndefinedBehaviorSanitizer: each -fsanitize= is given to the host compilation alone
+# (-Xarch_host), device code is built as usual. For the CPU tests of the C ABI, which run no
+# kernel: point GQA_LIBRARY_PATH at this library and preload clang's ASan runtime (see README).
+SANITIZED_LIBRARY = os.path.join(PKG, "libgqa_sanitized.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -51,20 +60,23 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(resource_usage: bool = False, jobs: int = 6) -> str:
-    """Compile every HIP source and link libgqa.so. Returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+def build(resource_usage: bool = False, jobs: int = 6, sanitize: bool = False) -> str:
+    """Compile every HIP source and link libgqa.so (with sanitize: libgqa_sanitized.so, host code
+    under ASan and UBSan). Returns the library path."""
+    build_dir = BUILD_DIR + ("_sanitized" if sanitize else "")
+    library = SANITIZED_LIBRARY if sanitize else LIBRARY
+    os.makedirs(build_dir, exist_ok=True)
+    extra = (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []) + (SANITIZE_FLAGS if sanitize else [])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIBRARY + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = library + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
+    return library
 
 
 if __name__ == "__main__":
-    print(build(resource_usage="--resource-usage" in sys.argv))
+    print(build(resource_usage="--resource-usage" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -30,19 +30,26 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _fp = ctypes.POINTER(ctypes.c_float)
 
 
-def compile_c(src: str, out: str) -> str:
+# A sanitized build (AddressSanitizer + UndefinedBehaviorSanitizer, gcc) of the same source, for
+# the CPU test suite run under those checkers: build it with build(sanitize=True) and point
+# GQA_ORACLE_LIBRARY at it (the process must preload gcc's libasan and libubsan; see README).
+SANITIZED_LIBRARY = os.path.join(_HERE, "liboracle_sanitized.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def compile_c(src: str, out: str, sanitize: bool = False) -> str:
     """gcc -O2 -fopenmp (no fast-math) of one oracle source into a shared library."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra",
-           "-o", tmp, src, "-lm"]
+           *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
 
 
-def build() -> str:
-    """Compile liboracle.so from gqa_oracle.c."""
-    return compile_c(SOURCE, LIBRARY)
+def build(sanitize: bool = False) -> str:
+    """Compile liboracle.so (or, with sanitize, liboracle_sanitized.so) from gqa_oracle.c."""
+    return compile_c(SOURCE, SANITIZED_LIBRARY if sanitize else LIBRARY, sanitize)
 
 
 def _f64(x) -> np.ndarray:
@@ -322,12 +329,16 @@ _default = None
 
 
 def load() -> Oracle:
-    """The oracle built from gqa_oracle.c (compiled here if missing or stale)."""
+    """The oracle built from gqa_oracle.c (compiled here if missing or stale), or the build that
+    GQA_ORACLE_LIBRARY names (the sanitized one)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
-            build()
-        _default = Oracle(LIBRARY)
+        path = os.environ.get("GQA_ORACLE_LIBRARY")
+        if path is None:
+            path = LIBRARY
+            if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+                build()
+        _default = Oracle(path)
     return _default
 
 
