@@ -600,7 +600,8 @@ def _summaries(args):
         if not cal:
             sys.exit("record the copy calibration first (--summarize-calibration)")
         res = summarize_counters(fetch_csv, write_csv, args.steps)
-        res = {n: r for n, r in res.items() if "stream_read" not in n}  # the cache flush
+        # The library's kernels of one call; not the cache flush, not torch's set-up kernels.
+        res = {n: r for n, r in res.items() if "gqa::" in n and "stream_read" not in n}
         total = sum(r["fetch_kib_median"] * 1024 * cal["fetch_scale"] + r["write_kib_median"] * 1024 * cal["write_scale"]
                     for r in res.values())
         family = "prefill" if "prefill" in args.workload else "decode"
