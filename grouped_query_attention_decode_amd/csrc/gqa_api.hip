@@ -128,8 +128,11 @@ DecodePlan plan_decode(int B, int H, int G, int D, int T_cap, int kv_dtype, int 
         p.flat = 1;
         p.pad = flat_pad_rows(D, kv_dtype);
         // One workgroup per CU: each streams a long run of rows, so the per-piece fixed costs
-        // (lengths, first block, merge) stay small against it.
-        p.nw = kNominalCUs;
+        // (lengths, first block, merge) stay small against it. INT4 caches take two per CU: their
+        // blocks are bound by the widening arithmetic of one wave per SIMD, which a second
+        // workgroup overlaps (ragged Llama-70B batch, 256 / 512 / 768 workgroups: INT4 19.8 /
+        // 18.0 / 18.7 us, in 16-row pages 21.8 / 20.1 / 20.9 us; bf16 33.4 / 34.6 / 39.9 us).
+        p.nw = kv_dtype == DT_INT4 ? 2 * kNominalCUs : kNominalCUs;
         const long per_slot = R * (D + 2) * (long)sizeof(float);
         const long fuse_slots = (long)kFuseMaxBytes / per_slot;
         const long full_chunk = ((long)B * G * T_cap + p.nw - 1) / p.nw;  // rows per workgroup, full caches
