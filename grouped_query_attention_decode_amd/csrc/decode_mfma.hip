@@ -575,6 +575,18 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         }
     }
 
+    // The next piece's query and first block are requested as soon as this piece's last block
+    // is in registers, so that their round trip overlaps the merge of the waves, the partial
+    // stores and the arrival. (Above 32 heads per KV head the caller loads them after the
+    // return: the accumulators and the next block together would spill.)
+    if constexpr (NHB <= 2) {
+        if (np.valid) {
+            load_q<NHB, KV>(qT, np.q, R, lane);
+            const int t0n = np.kb + wave * kBlockT;
+            if (t0n < np.ke) load_block<KV, PAGED>(nxt, np.src, fetch_pages<PAGED>(np.src, t0n), t0n, np.ke, lane);
+        }
+    }
+
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
     // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
     // slice; every thread then sums four slices for 4 consecutive head dims.
@@ -635,20 +647,10 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             }
         }
     }
-    auto prefetch_next = [&] {
-        if (np.valid) {
-            load_q<NHB, KV>(qT, np.q, R, lane);
-            const int t0n = np.kb + wave * kBlockT;
-            if (t0n < np.ke) load_block<KV, PAGED>(nxt, np.src, fetch_pages<PAGED>(np.src, t0n), t0n, np.ke, lane);
-        }
-    };
     if (!po.direct && a.fuse_combine) {
         if (splitkv_arrive(a.counters + bg, po.n_slots))
             splitkv_merge_bf16<kThreads, kD>(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
     }
-    // (Above 32 heads per KV head the caller loads them after the return: the registers of
-    // the last-arriver merge and the next block together would spill.)
-    if constexpr (NHB <= 2) prefetch_next();
 }
 
 // The rows of (sequence b, KV head g): a slab of the contiguous cache, or the page pools and
@@ -682,7 +684,6 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
-    constexpr int RBL = kLdsRowBytes<KV>;
     constexpr int LDS_BYTES = kLdsBytes<KV, NHB>;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
@@ -750,7 +751,6 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
     constexpr int HP = 16 * NHB;
-    constexpr int RBL = kLdsRowBytes<KV>;
     constexpr int LDS_BYTES = kLdsBytes<KV, NHB>;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
