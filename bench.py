@@ -82,6 +82,26 @@ EXTRA_WORKLOADS = {
     "gqa8_chunked_prefill_B4_Tq512_L4096_fp8": W.chunked_prefill_512_of_4096_fp8,
 }
 
+# Breakdown entries derived from the named workloads: the cache append done by the decode call
+# itself ("+append"), and the caches scattered into shuffled pages of 16 rows ("_paged16").
+# Selectable with --workload too, so that their counters can be recorded like the others'.
+APPEND_DECODES = ("llama70b_gqa8_decode_B16_ragged", "llama7b_gqa8_decode_L2048", "mqa_fp8_decode_B8_L32768")
+PAGED_DECODES = ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768")
+PAGED_CHUNK = "gqa8_chunked_prefill_B4_Tq512_L4096"
+DERIVED_WORKLOADS = ([n + "+append" for n in APPEND_DECODES] + [n + "_paged16" for n in PAGED_DECODES]
+                     + [PAGED_CHUNK + "_paged16"])
+
+
+def derived_case(name):
+    """(case, append) of a derived workload name."""
+    if name.endswith("+append"):
+        return W.WORKLOADS[name[:-len("+append")]](0), True
+    base = name[:-len("_paged16")]
+    if base == PAGED_CHUNK:
+        return W.make_paged_chunk(W.chunked_prefill_512_of_4096(0), 16, seed=1), False
+    return W.make_paged(W.WORKLOADS[base](0), 16, seed=1), False
+
+
 # Narrow-group decodes (R = 2, 4, 8 query heads per KV head) for the comparison of the
 # vector-ALU and matrix-core kernel families (--workload with --path); not in the breakdown.
 NARROW_WORKLOADS = {
@@ -360,7 +380,7 @@ def bench_decode(gqa, c, steps, warmup, dev, flush, append=False, path="auto"):
         "eager_us_per_call": t["eager_ms_per_call"] * 1e3, "timing": t["timing"], "replicas": nrep,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if append or isinstance(c, W.PagedDecodeCase) else measured_traffic(c.name)},
+                     "traffic": measured_traffic(c.name + ("+append" if append else ""))},
     }
 
 
@@ -621,7 +641,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE,
-                    choices=[k for k in W.WORKLOADS if k != "toy"] + list(EXTRA_WORKLOADS) + list(NARROW_WORKLOADS))
+                    choices=[k for k in W.WORKLOADS if k != "toy"] + list(EXTRA_WORKLOADS) + list(NARROW_WORKLOADS)
+                    + DERIVED_WORKLOADS)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "generic"],
                     help="decode kernel family for --workload (the breakdown always runs auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -677,6 +698,11 @@ def main():
         return r
 
     def run(name, steps, warmup, append=False, path="auto"):
+        if name in DERIVED_WORKLOADS:
+            case, append = derived_case(name)
+            if not append:
+                return case, run_case(case, steps, warmup)
+            name = case.name
         case = (W.WORKLOADS.get(name) or EXTRA_WORKLOADS.get(name) or NARROW_WORKLOADS[name])(0)
         if path != "auto" and isinstance(case, W.DecodeCase):
             log(f"[bench] {name} path={path}: steps={steps} warmup={warmup}")
@@ -703,22 +729,18 @@ def main():
                 continue
             _, breakdown[name] = run(name, small_steps, small_warmup)
         # The decode step with the current token's cache append done by the same call.
-        for name in dict.fromkeys((args.workload, "llama7b_gqa8_decode_L2048", "mqa_fp8_decode_B8_L32768")):
-            if isinstance((W.WORKLOADS.get(name) or EXTRA_WORKLOADS.get(name) or NARROW_WORKLOADS[name])(0),
-                          W.DecodeCase):
+        for name in APPEND_DECODES:
+            if name + "+append" != args.workload:
                 _, breakdown[name + "+append"] = run(name, small_steps, small_warmup, append=True)
         # INT4 caches (4-bit fields, one scale per sequence and KV head), and prefill of a
         # 512-token chunk against a 3584-token cache.
         for name in EXTRA_WORKLOADS:
             if name != args.workload:
                 _, breakdown[name] = run(name, small_steps, small_warmup)
-        # The chunked prefill against the same cache in shuffled pages of 16 rows.
-        pcc = W.make_paged_chunk(W.chunked_prefill_512_of_4096(0), 16, seed=1)
-        breakdown[pcc.name] = run_case(pcc, small_steps, small_warmup)
-        # The same decodes over a cache in shuffled pages of 16 rows.
-        for name in ("llama7b_gqa8_decode_L2048", "llama70b_gqa8_decode_B16_ragged", "mqa_fp8_decode_B8_L32768"):
-            pc = W.make_paged(W.WORKLOADS[name](0), 16, seed=1)
-            breakdown[pc.name] = run_case(pc, small_steps, small_warmup)
+        # The chunked prefill, and the decodes, against the same caches in shuffled pages of 16 rows.
+        for name in [PAGED_CHUNK + "_paged16"] + [n + "_paged16" for n in PAGED_DECODES]:
+            if name != args.workload:
+                _, breakdown[name] = run(name, small_steps, small_warmup)
 
     achievable = hbm_achievable(gqa, flush)
     del flush
@@ -742,9 +764,9 @@ def main():
     else:
         value, unit = head["kv_read_GBps"], "GB/s"
         dtype = {W.BF16: "bf16", W.FP8: "fp8_e4m3fn", W.F32: "f32", W.INT4: "int4"}[case.kv_dtype]
-    cfg = {"workload": case.name, "global_batch": case.B, "heads": case.H, "kv_heads": case.G,
+    cfg = {"workload": args.workload, "global_batch": case.B, "heads": case.H, "kv_heads": case.G,
            "head_dim": case.D, "parallelism": "none (1 GPU)"}
-    if isinstance(case, W.ChunkCase):
+    if isinstance(case, (W.ChunkCase, W.PagedChunkCase)):
         cfg["seq_len"], cfg["chunk_len"] = case.T_cap, case.Tq
     elif is_prefill:
         cfg["seq_len"] = case.T

@@ -76,6 +76,16 @@ def test_chunk_flops_brute_force(causal):
     assert bench.chunk_flops(c) == 4 * 4 * 8 * pairs
 
 
+def test_derived_workloads_resolve():
+    c, append = bench.derived_case("llama7b_gqa8_decode_L2048+append")
+    assert isinstance(c, W.DecodeCase) and append and c.name == "llama7b_gqa8_decode_L2048"
+    c, append = bench.derived_case("llama7b_gqa8_decode_L2048_paged16")
+    assert isinstance(c, W.PagedDecodeCase) and not append and c.name == "llama7b_gqa8_decode_L2048_paged16"
+    # the traffic key of a derived entry is its name
+    assert {"llama7b_gqa8_decode_L2048+append", "llama7b_gqa8_decode_L2048_paged16",
+            "gqa8_chunked_prefill_B4_Tq512_L4096_paged16"} <= set(bench.DERIVED_WORKLOADS)
+
+
 # ---- rocprofv3 summaries ---------------------------------------------------------------
 
 def _write_csv(path, fieldnames, rows):
