@@ -637,8 +637,8 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             const f32x4_t v = {acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale};
             if (a.fuse_combine)  // whole 16-byte chunks: every wave store writes full lines
                 splitkv_store4c(splitkv_acc_rsrc(a, head0, R), (unsigned)(((h * S + po.slot) * kD + d) * 4), v);
-            else
-                *(f32x4_t *)&a.part_acc[((head0 + h) * S + po.slot) * kD + d] = v;
+            else  // read once, by the combine kernel: streamed past the caches (fp8 MQA decode -0.8 us)
+                __builtin_nontemporal_store(v, (f32x4_t *)&a.part_acc[((head0 + h) * S + po.slot) * kD + d]);
             if (d == 0) {
                 float M = m_w[0][h];
 #pragma unroll
