@@ -106,10 +106,12 @@ constexpr int kFlatMinBatch = 16;
 // its partials and arrival: a few microseconds at the ~27 GB/s one CU streams) as the K/V bytes
 // a workgroup would stream meanwhile, and as rows of a cache type. Measured on the ragged
 // Llama-70B batch (pads of 0 / 40 / 80 / 120 / 160 / 240 KiB): bf16 35.4 / 34.9 / 34.6 / 33.7 /
-// 33.8 / 34.0 us; its INT4 cache 20.9 / 20.1 / 19.7 / 20.0 / 20.6 / 22.5 us; a ragged fp8 MQA
-// batch (B16 H32 G1, 2k-16k keys) 26.0 / 23.9 / 22.2 / 21.5 / 21.5 / 21.3 us.
+// 33.8 / 34.0 us; a ragged fp8 MQA batch (B16 H32 G1, 2k-16k keys) 26.0 / 23.9 / 22.2 / 21.5 /
+// 21.5 / 21.3 us. Again with the next piece requested before the wave merge: bf16 at 80 / 100 /
+// 120 / 140 / 170 KiB 34.2 / 34.1 / 33.0 / 33.4 / 33.7 us; the INT4 cache (two workgroups per
+// CU) at 50 / 65 / 80 / 95 / 115 KiB 17.9 / 17.6 / 18.2 / 18.4 / 18.4 us.
 int flat_pad_rows(long D, int kv_dtype) {
-    const long cost = kv_dtype == DT_INT4 ? 80 * 1024 : 120 * 1024;
+    const long cost = kv_dtype == DT_INT4 ? 64 * 1024 : 120 * 1024;
     return (int)(cost / (2 * row_bytes(kv_dtype, D)));
 }
 
