@@ -176,6 +176,18 @@ def test_decode_cases(gqa, B, H, G, D, lens, T_cap, qd, kvd):
     run_all_paths(gqa, c, oracle.decode(c), splits=(0, 1, 3))
 
 
+@pytest.mark.parametrize("B,kvd", [(256, W.BF16), (257, W.BF16), (600, W.BF16), (600, W.FP8), (300, W.INT4)])
+def test_decode_flat_large_batches(gqa, B, kvd):
+    """The flat layout past the 256 lengths a workgroup keeps in LDS: from 257 sequences on, the
+    lengths, the first segment of a run and every later segment are read from memory. Ragged
+    lengths 1..120 with empty sequences between them."""
+    lens = [0 if i % 13 == 5 else (i * 29) % 120 + 1 for i in range(B)]
+    c = W.make_decode(B, 8, 2, 128, lens, T_cap=128, kv_dtype=kvd, seed=B + 5, name=f"flat_B{B}")
+    want = oracle.decode(c)
+    for layout in ("flat", "auto"):
+        check(dev_decode(gqa, c, layout=layout), want, TOL.get(kvd, 5e-2), f"{c.name} {kvd} layout={layout}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 64, 1024])
 def test_decode_forced_splits(gqa, splits):
     """Split counts from one to far more than there are keys (empty splits)."""
