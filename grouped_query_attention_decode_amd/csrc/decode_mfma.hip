@@ -17,17 +17,20 @@
 //
 // Per 32-token block, per wave:
 //   S^T (32 tokens x 16 heads per head block) = K . Q^T          -- 16x16x32 bf16 MFMA
-//        K rows go from HBM straight into the MFMA A-operand layout (16-byte loads);
-//        rows are assigned to MFMA rows so that afterwards each lane holds 8 consecutive
-//        tokens of one head, which is exactly the B-operand layout of the next product.
+//        K rows are loaded whole (four bf16 or eight fp8 rows per wave instruction), written
+//        to a wave-private LDS tile and read back in the MFMA A-operand layout (an INT4 row
+//        is 64 bytes, one operand row: loaded straight into registers); rows are assigned to
+//        MFMA rows so that afterwards each lane holds 8 consecutive tokens of one head,
+//        which is exactly the B-operand layout of the next product.
 //   online softmax in base 2 (scale * log2(e) * k_scale applied to the fp32 scores)
 //   O^T (128 d x 16 heads) += V^T . P^T                          -- 16x16x32 bf16 MFMA
 //        V rows are loaded coalesced (4 rows of 256 bytes per wave instruction), written to
 //        a wave-private LDS tile, and read back transposed with ds_read_b64_tr_b16
 //        (ds_read_b64_tr_b8 + exact fp8->bf16 widening for fp8; INT4 rows are widened to
 //        bf16 on their way into the tile, and K fields straight into the operands).
-// Tokens at or beyond the valid length are masked by index; their rows are never loaded
-// (the load index is clamped to the last valid row, and their probabilities are zero).
+// Tokens at or beyond the valid length are masked by index and their values zeroed: a wave's
+// first block is requested before the length is known (rows clamped to the allocation), the
+// later ones clamp their rows to the last row of the range.
 // v_scale multiplies the output once, in the epilogue.
 // With a cache append, the wave whose block holds the last valid row swaps the caller's new
 // key/value (quantised for fp8) into its registers and stores that row: no separate pass.
@@ -803,11 +806,13 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     const int N = G * Ng;
 
     if (blockIdx.x == 0 && a.fuse_combine) {
-        // Sequences without keys belong to no piece: their output rows are zero.
+        // Sequences without keys belong to no piece: their output rows are zero. (From the
+        // lengths in LDS where they are cached: no round trip before this workgroup's loads.)
         uint16_t *out = static_cast<uint16_t *>(a.out);
         for (int k0 = 0; k0 < B; k0 += 64) {
             const int bb = k0 + lane;
-            unsigned long long empty = __ballot(bb < B && clamp_len(a.seq_lens[bb], a.Tk) == 0);
+            const int t = bb < B ? clamp_len(B <= kLenCache ? len_s[bb] : a.seq_lens[bb], a.Tk) : 1;
+            unsigned long long empty = __ballot(t == 0);
             while (empty) {
                 const int be = k0 + __ffsll((long long)empty) - 1;
                 empty &= empty - 1;
@@ -815,7 +820,6 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
             }
         }
     }
-
     const int xe = (int)blockIdx.x * C + C < N ? (int)blockIdx.x * C + C : N;
     int g = gb0 / B, b = gb0 % B;
 
