@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -111,14 +112,23 @@ NARROW_WORKLOADS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source text without its comments, every run of white space made one space: what
+    the kernels are built from, whatever the wording or layout of the comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_sources_sha256(family: str) -> str:
-    """Hash of the sources of one kernel family; counters taken on other sources do not apply."""
+    """Hash of the code (comments left out) of one kernel family's sources; counters taken on
+    other code do not apply."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(_FAMILY_SOURCES[family]):
         h.update(name.encode())
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

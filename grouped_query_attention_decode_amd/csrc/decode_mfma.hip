@@ -303,7 +303,8 @@ struct PieceOut {
 
 // The piece a workgroup of the flat layout takes up after the current one. Its query and this
 // wave's first block of it are requested into the registers the current piece no longer needs
-// (qT, nxt) as soon as the current piece's results are out, before the workgroup leaves attend().
+// (qT, nxt) as soon as the current piece's last block is in registers, before the merge of the
+// waves.
 struct NextPiece {
     KvSrc src;
     const uint16_t *q;  // its R query heads

@@ -155,6 +155,23 @@ def test_recorded_traffic_goes_stale_when_the_sources_change(tmp_path, monkeypat
     assert bench.measured_traffic("w_decode") is None
 
 
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    monkeypatch.setattr(bench, "CSRC", str(src))
+    monkeypatch.setattr(bench, "_FAMILY_SOURCES", {"decode": ("k.hip", "h.h")})
+    (src / "h.h").write_text("#pragma once\nconstexpr int kN = 4;  // four\n")
+    (src / "k.hip").write_text("/* a kernel */\nint f(int x) { return x + kN; }  // plus\n")
+    h0 = bench.kernel_sources_sha256("decode")
+    (src / "k.hip").write_text("/* the same kernel,\n   other words */\nint f(int x) { return x + kN; }\n// done\n")
+    assert bench.kernel_sources_sha256("decode") == h0
+    (src / "k.hip").write_text("/* a kernel */\nint f(int x) { return x - kN; }  // plus\n")
+    assert bench.kernel_sources_sha256("decode") != h0
+    (src / "k.hip").write_text("/* a kernel */\nint f(int x) { return x + kN; }  // plus\n")
+    (src / "h.h").write_text("#pragma once\nconstexpr int kN = 5;  // four\n")
+    assert bench.kernel_sources_sha256("decode") != h0
+
+
 def test_committed_traffic_records_name_their_sources():
     with open(bench.TRAFFIC_FILE) as f:
         rec = json.load(f)
