@@ -590,6 +590,91 @@ def summarize_counters(fetch_csv, write_csv, steps):
     return out
 
 
+# ------------------------------------------------------------------------------------
+# Per-workgroup timeline of a decode (the diagnostic timeline build of the library).
+# ------------------------------------------------------------------------------------
+
+def timeline_summary(stamps, label):
+    """Text summary of one decode call's per-workgroup timeline: per phase, the 0/10/50/90/100th
+    percentiles over the workgroups, in microseconds from the first workgroup's entry (slots as
+    described in include/gqa_measure.h; the clock runs at 100 MHz)."""
+    import numpy as np
+    a = stamps.astype(np.int64)
+    used = np.nonzero(a[:, 0])[0]
+    if len(used) == 0:
+        return [f"== {label}: no stamps"]
+    a = a[:int(used.max()) + 1]
+    nwg = a.shape[0]
+    t0 = a[:, 0].min()
+    us = lambda col: (a[:, col] - t0) * 0.01
+    pc = lambda x: " ".join(f"{v:6.2f}" for v in np.percentile(x, [0, 10, 50, 90, 100])) if len(x) else "-"
+    n = a[:, 21]
+    ok = n > 0
+    last = 2 + 6 * np.clip(n - 1, 0, 2)
+    idx = np.arange(nwg)
+    at = lambda off: (a[idx, last + off] - t0) * 0.01
+    arrived = a[idx, last + 4] != 0
+    exit_ = us(20)
+    out = [f"== {label}: {nwg} workgroups, span {exit_.max():.2f} us (first entry to last exit)",
+           f"  {'phase (us from the first entry)':44s}    p0    p10    p50    p90   p100",
+           f"  {'entry':44s} {pc(us(0))}",
+           f"  {'length(s) / layout known':44s} {pc(us(1))}",
+           f"  {'first piece: first block done':44s} {pc(us(3)[a[:, 3] != 0])}",
+           f"  {'last piece: block loop done':44s} {pc(at(2)[ok])}",
+           f"  {'exit':44s} {pc(exit_[ok])}",
+           f"  {'last piece, durations:':44s}",
+           f"  {'  block loop done -> exit':44s} {pc((exit_ - at(2))[ok])}",
+           f"  {'  merge of the waves, partials issued':44s} {pc((at(3) - at(2))[ok])}",
+           f"  {'  arrival counted (split ranges)':44s} {pc((at(4) - at(3))[ok & arrived])}",
+           f"  {'  then to the end (last arriver: its merge)':44s} "
+           f"{pc((at(5) - np.where(arrived, at(4), at(3)))[ok])}"]
+    for k in (1, 2, 3):
+        m = n == k
+        if m.any():
+            out.append(f"  workgroups with {k} piece(s): {int(m.sum()):4d}, exit median {np.median(exit_[m]):6.2f} "
+                       f"max {exit_[m].max():6.2f}")
+    out.append("  by blockIdx mod 8 (the XCD the dispatcher sends it to): exit median / max, last loop done median")
+    for x in range(8):
+        m = ((idx % 8) == x) & ok
+        if m.any():
+            out.append(f"    {x}: {np.median(exit_[m]):6.2f} / {exit_[m].max():6.2f}   {np.median(at(2)[m]):6.2f}")
+    return out
+
+
+def run_timeline(args):
+    """--timeline: cold decode calls of --workload on the timeline build, one summary each."""
+    from grouped_query_attention_decode_amd import build as B
+    import grouped_query_attention_decode_amd as gqa
+    if "GQA_LIBRARY_PATH" not in os.environ:
+        gqa.LIBRARY_PATH = B.TIMELINE_LIBRARY
+    if not os.path.exists(gqa.LIBRARY_PATH):
+        sys.exit(f"{gqa.LIBRARY_PATH} is not built: python -m grouped_query_attention_decode_amd.build --timeline")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gqa.library()
+    case = (W.WORKLOADS.get(args.workload) or EXTRA_WORKLOADS.get(args.workload) or
+            NARROW_WORKLOADS.get(args.workload) or (lambda s: None))(0)
+    if not isinstance(case, W.DecodeCase):
+        sys.exit("--timeline takes a contiguous decode workload")
+    flush = Flusher(gqa, dev)
+    q, k, v, lens = case.q.to(dev), case.k_cache.to(dev), case.v_cache.to(dev), case.seq_lens.to(dev)
+    ks = case.k_scale.to(dev) if case.k_scale is not None else None
+    vs = case.v_scale.to(dev) if case.v_scale is not None else None
+    need = gqa.decode_workspace_size(case.B, case.H, case.G, case.D, case.T_cap, case.kv_dtype)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    call = lambda: gqa.decode(q, k, v, lens, out=out, scale=case.scale, k_scale=ks, v_scale=vs, workspace=ws)
+    for _ in range(max(args.warmup, 3)):
+        call()
+    torch.cuda.synchronize()
+    for r in range(args.steps):
+        gqa.timeline_clear()
+        flush()
+        call()
+        torch.cuda.synchronize()
+        print("\n".join(timeline_summary(gqa.timeline_read(), f"{case.name}, cold call {r}")), flush=True)
+
+
 def _summaries(args):
     """The --summarize-* modes: read rocprofv3 CSV output, print (and for counters record) the
     figures kept under profiles/. No GPU needed."""
@@ -667,6 +752,9 @@ def main():
                     help="record HBM traffic per launch of --workload in profiles/traffic.json")
     ap.add_argument("--summarize-calibration", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="record the counter scale of a --copy-calibration run in profiles/traffic.json")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timeline of --steps cold calls of a decode --workload (needs the "
+                         "timeline build: python -m grouped_query_attention_decode_amd.build --timeline)")
     args = ap.parse_args()
     if args.summarize_trace or args.summarize_counters or args.summarize_calibration or args.summarize_pmc:
         return _summaries(args)
@@ -678,6 +766,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.timeline:
+        return run_timeline(args)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)

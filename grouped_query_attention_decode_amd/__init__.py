@@ -108,6 +108,10 @@ def library() -> ctypes.CDLL:
     lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
     lib.gqa_hbm_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.gqa_hbm_stream_read.restype = i
+    lib.gqa_timeline_read.argtypes = [vp, ctypes.c_size_t]
+    lib.gqa_timeline_read.restype = i
+    lib.gqa_timeline_clear.argtypes = []
+    lib.gqa_timeline_clear.restype = i
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     runtimes = _hip_runtimes_mapped()
@@ -145,6 +149,28 @@ def hbm_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
                                        _stream_handle(stream, buf.device))
     if st != GQA_OK:
         raise GqaError(st, "gqa_hbm_stream_read")
+
+
+TIMELINE_WORKGROUPS, TIMELINE_SLOTS = 4096, 32
+
+
+def timeline_clear() -> None:
+    """Zero the per-workgroup timeline (gqa_timeline_clear; the timeline build only)."""
+    st = library().gqa_timeline_clear()
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_timeline_clear")
+
+
+def timeline_read():
+    """The per-workgroup timeline of the decode kernels since the last clear, as a numpy uint64
+    array [4096 workgroups, 32 slots] (gqa_timeline_read; the timeline build only; the slots are
+    described in include/gqa_measure.h)."""
+    import numpy as np
+    buf = np.zeros((TIMELINE_WORKGROUPS, TIMELINE_SLOTS), dtype=np.uint64)
+    st = library().gqa_timeline_read(buf.ctypes.data, buf.nbytes)
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_timeline_read")
+    return buf
 
 
 def decode_num_splits(B, H, G, D, kv_capacity, kv_dtype="bf16", num_splits=0) -> int:

@@ -45,6 +45,9 @@ CFLAGS = [
 # (-Xarch_host), device code is built as usual. For the CPU tests of the C ABI, which run no
 # kernel: point GQA_LIBRARY_PATH at this library and preload clang's ASan runtime (see README).
 SANITIZED_LIBRARY = os.path.join(PKG, "libgqa_sanitized.so")
+# Diagnostic build: the decode kernels record per-workgroup timestamps (gqa_timeline_read in
+# include/gqa_measure.h). Never the library the binding loads by default.
+TIMELINE_LIBRARY = os.path.join(PKG, "libgqa_timeline.so")
 SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                   "-Xarch_host", "-fno-omit-frame-pointer"]
 
@@ -60,13 +63,16 @@ def _compile(src: str, extra, build_dir: str) -> str:
     return obj
 
 
-def build(resource_usage: bool = False, jobs: int = 6, sanitize: bool = False) -> str:
+def build(resource_usage: bool = False, jobs: int = 6, sanitize: bool = False, timeline: bool = False) -> str:
     """Compile every HIP source and link libgqa.so (with sanitize: libgqa_sanitized.so, host code
-    under ASan and UBSan). Returns the library path."""
-    build_dir = BUILD_DIR + ("_sanitized" if sanitize else "")
-    library = SANITIZED_LIBRARY if sanitize else LIBRARY
+    under ASan and UBSan; with timeline: libgqa_timeline.so, the decode kernels stamping
+    per-workgroup times). Returns the library path."""
+    assert not (sanitize and timeline)
+    build_dir = BUILD_DIR + ("_sanitized" if sanitize else "_timeline" if timeline else "")
+    library = SANITIZED_LIBRARY if sanitize else TIMELINE_LIBRARY if timeline else LIBRARY
     os.makedirs(build_dir, exist_ok=True)
-    extra = (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []) + (SANITIZE_FLAGS if sanitize else [])
+    extra = (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []) + (SANITIZE_FLAGS if sanitize else []) \
+        + (["-DGQA_TIMELINE"] if timeline else [])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
     tmp = library + ".tmp"
@@ -79,4 +85,5 @@ def build(resource_usage: bool = False, jobs: int = 6, sanitize: bool = False) -
 
 
 if __name__ == "__main__":
-    print(build(resource_usage="--resource-usage" in sys.argv, sanitize="--sanitize" in sys.argv))
+    print(build(resource_usage="--resource-usage" in sys.argv, sanitize="--sanitize" in sys.argv,
+                timeline="--timeline" in sys.argv))

@@ -36,10 +36,31 @@
 // key/value (quantised for fp8) into its registers and stores that row: no separate pass.
 #include "dtypes.h"
 #include "gqa_internal.h"
+#include "gqa_measure.h"
 #include "mfma_util.h"
 #include "splitkv.h"
 
 namespace gqa {
+
+// ---- Per-workgroup timeline (diagnostic build only) ----
+// Built with GQA_TIMELINE (libgqa_timeline.so: build.py --timeline), thread 0 of every
+// workgroup records the device's constant 100 MHz clock (s_memrealtime) at fixed points of
+// the decode kernels into g_timeline[workgroup][slot]; in the library proper every stamp is
+// empty. Slots: 0 entry; 1 length(s) and work layout known; for piece p < 3 of the workgroup,
+// 2 + 6 p + {0 start, 1 first block done, 2 block loop done (both wave 0), 3 waves merged and
+// partials issued, 4 arrival counted, 5 end}; 20 exit; 21 number of pieces (a count).
+#ifdef GQA_TIMELINE
+constexpr int kTlWorkgroups = 4096, kTlSlots = 32;
+__device__ unsigned long long g_timeline[kTlWorkgroups * kTlSlots];
+__device__ __forceinline__ void tl_put(int slot, unsigned long long v) {
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kTlWorkgroups && slot >= 0 && slot < kTlSlots)
+        g_timeline[blockIdx.x * kTlSlots + slot] = v;
+}
+__device__ __forceinline__ void tl_stamp(int slot) { tl_put(slot, __builtin_amdgcn_s_memrealtime()); }
+#else
+__device__ __forceinline__ void tl_put(int, unsigned long long) {}
+__device__ __forceinline__ void tl_stamp(int) {}
+#endif
 
 namespace {
 
@@ -47,8 +68,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockT = 32;  // tokens per wave iteration
 constexpr int kD = 128;
-constexpr int kDP = kD + 4;
-constexpr int kLenCache = 256;  // flat layout: sequence lengths kept in LDS for batches up to this  // row stride of the wave-merge tile: rows of 16 heads on distinct LDS banks
+constexpr int kDP = kD + 4;      // row stride of the wave-merge tile: rows of 16 heads on distinct LDS banks
+constexpr int kLenCache = 256;  // flat layout: sequence lengths kept in LDS for batches up to this
 
 // MFMA row m of token sub-block `blk` (0/1) holds token tau(blk, m) of the 32-token block,
 // so that C row 4*(l/16)+i of both sub-blocks lands in lane l as tokens 8*(l/16) + 4*blk + i.
@@ -299,6 +320,7 @@ struct PieceOut {
     int n_slots;  // key ranges of this (sequence, KV head) that hold keys
     bool direct;  // the range covers the whole sequence: write the output itself
     bool append;  // the range ends at the sequence's last row, which the new token fills
+    int seq = 0;  // its place among the workgroup's pieces (timeline build)
 };
 
 // The piece a workgroup of the flat layout takes up after the current one. Its query and this
@@ -322,6 +344,8 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                                        i32x4_t (&qT)[NHB][4], Frag<KV> &nxt, const KvSrc &src, float c,
                                        float vscale, const NextPiece &np) {
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
+    const int tls = 2 + 6 * (po.seq < 3 ? po.seq : 2);  // timeline slots of this piece
+    tl_stamp(tls);
     constexpr int RBL = kLdsRowBytes<KV>;  // V-tile row bytes in LDS
     constexpr int VT = kBlockT * RBL;      // V tile bytes per wave
     constexpr int HP = 16 * NHB;           // heads padded to MFMA blocks
@@ -558,10 +582,14 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     if (t0 < ke) {
         // The wave's last block is peeled off the loop: it is the one that may hold the row
         // of a cache append, and code for that kept out of the loop costs it no registers.
-        const int tl = t0 + (ke - 1 - t0) / kStep * kStep;
-        for (; t0 < tl; t0 += kStep) step(nxt, t0, kStep, std::false_type{});
-        if (po.append && tl + kBlockT >= ke) append_row<KV, PAGED>(nxt, a, bg, src, tl, ke - 1, lane);
-        step(nxt, tl, 0, std::true_type{});
+        const int tlast = t0 + (ke - 1 - t0) / kStep * kStep;
+        for (; t0 < tlast; t0 += kStep) {
+            step(nxt, t0, kStep, std::false_type{});
+            if (t0 == kb) tl_stamp(tls + 1);
+        }
+        if (po.append && tlast + kBlockT >= ke) append_row<KV, PAGED>(nxt, a, bg, src, tlast, ke - 1, lane);
+        step(nxt, tlast, 0, std::true_type{});
+        if (tlast == kb) tl_stamp(tls + 1);
     }
     if constexpr (I4) {
         // Take 136 * sum(p) out of every output: o held sum_t p_t (136 + code_t) v_scale-free.
@@ -579,6 +607,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         }
     }
 
+    tl_stamp(tls + 2);
     // The next piece's query and first block are requested as soon as this piece's last block
     // is in registers, so that their round trip overlaps the merge of the waves, the partial
     // stores and the arrival. (Above 32 heads per KV head the caller loads them after the
@@ -651,10 +680,13 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             }
         }
     }
+    tl_stamp(tls + 3);
     if (!po.direct && a.fuse_combine) {
-        if (splitkv_arrive(a.counters + bg, po.n_slots))
-            splitkv_merge_bf16<kThreads, kD>(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
+        const bool last = splitkv_arrive(a.counters + bg, po.n_slots);
+        tl_stamp(tls + 4);
+        if (last) splitkv_merge_bf16<kThreads, kD>(a, head0, R, po.n_slots, static_cast<uint16_t *>(a.out));
     }
+    tl_stamp(tls + 5);
 }
 
 // The rows of (sequence b, KV head g): a slab of the contiguous cache, or the page pools and
@@ -702,6 +734,7 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     const int b = bg / G, g = bg % G;
     const int kb = split * a.split_len;
     const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
+    tl_stamp(0);
 
     // The query, the scales and this wave's first block do not depend on the length (the
     // block's rows are clamped to the allocation), so they are requested before it and share
@@ -718,6 +751,7 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     const int Lraw = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     const int L = clamp_len(Lraw, a.Tk);
     const int ke = kb + a.split_len < L ? kb + a.split_len : L;
+    tl_stamp(1);
 
     if (kb >= ke) {  // nothing to attend to in this range
         // Fused merges count only non-empty ranges, so an empty one only has to produce the
@@ -731,6 +765,8 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
                 a.part_ml[((head0 + h) * S + split) * 2 + 1] = 0.f;
             }
         }
+        tl_stamp(20);
+        tl_put(21, 0);
         return;
     }
     PieceOut po;
@@ -742,6 +778,8 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     const NextPiece none = {};
     attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, kb, ke, po, qT, nxt, src,
                             a.scale_log2 * kscale, vscale, none);
+    tl_stamp(20);
+    tl_put(21, 1);
 }
 
 // Flat layout (splitkv.h): workgroup w streams rows [w C, (w + 1) C) of the concatenated
@@ -766,6 +804,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
     const int G = a.G, H = a.H, R = H / G, B = a.B;
+    tl_stamp(0);
 
     // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row. The
     // lengths are read from memory once (into LDS, for batches up to kLenCache; the search for
@@ -805,6 +844,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     const int gb0 = __builtin_amdgcn_readfirstlane(lay_s[2]);
     int Pb = __builtin_amdgcn_readfirstlane(lay_s[3]);
     const int N = G * Ng;
+    tl_stamp(1);
 
     if (blockIdx.x == 0 && a.fuse_combine) {
         // Sequences without keys belong to no piece: their output rows are zero. (From the
@@ -850,9 +890,18 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         }
     };
 
-    if ((int)blockIdx.x * C >= xe) return;
+    if ((int)blockIdx.x * C >= xe) {
+        tl_stamp(20);
+        tl_put(21, 0);
+        return;
+    }
     Piece cur = piece_at((int)blockIdx.x * C);
-    if (cur.ke <= cur.kb) return;  // the run holds pad rows only
+    if (cur.ke <= cur.kb) {  // the run holds pad rows only
+        tl_stamp(20);
+        tl_put(21, 0);
+        return;
+    }
+    int npieces = 0;
     i32x4_t qT[NHB][4];
     Frag<KV> nxt;
     {
@@ -870,6 +919,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         po.direct = po.n_slots == 1;
         // The length as stored (not clamped) decides whether row L-1 exists for an append.
         po.append = a.k_new && cur.ke == cur.Tb && __builtin_amdgcn_readfirstlane(a.seq_lens[cur.b]) == cur.Tb;
+        po.seq = npieces++;
         const float kscale = FP8 || I4 ? a.k_scale[bg] : 1.f;
         const float vscale = FP8 || I4 ? a.v_scale[bg] : 1.f;
         const KvSrc src = kv_src<PAGED, RB>(a, cur.b, cur.g, bg);
@@ -889,7 +939,11 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         }
         attend<NHB, KV, PAGED>(a, lds, m_w, l_w, lane, wave, head0, R, bg, cur.kb, cur.ke, po, qT, nxt, src,
                                a.scale_log2 * kscale, vscale, np);
-        if (!np.valid) break;
+        if (!np.valid) {
+            tl_stamp(20);
+            tl_put(21, (unsigned long long)npieces);
+            break;
+        }
         if constexpr (NHB > 2) {
             load_q<NHB, KV>(qT, np.q, R, lane);
             const int t0 = np.kb + wave * kBlockT;
@@ -941,3 +995,26 @@ hipError_t launch_decode_mfma(const AttnArgs &a, hipStream_t stream) {
 }
 
 }  // namespace gqa
+
+// Timeline access (gqa_measure.h): the library proper has no timeline and says so.
+extern "C" gqa_status gqa_timeline_read(void *dst, size_t bytes) {
+    if (!dst) return GQA_ERR_INVALID_ARG;
+#ifdef GQA_TIMELINE
+    const size_t all = sizeof(unsigned long long) * gqa::kTlWorkgroups * gqa::kTlSlots;
+    return hipMemcpyFromSymbol(dst, HIP_SYMBOL(gqa::g_timeline), bytes < all ? bytes : all) == hipSuccess
+               ? GQA_OK
+               : GQA_ERR_HIP;
+#else
+    (void)bytes;
+    return GQA_ERR_UNSUPPORTED;
+#endif
+}
+
+extern "C" gqa_status gqa_timeline_clear(void) {
+#ifdef GQA_TIMELINE
+    static const unsigned long long zeros[gqa::kTlWorkgroups * gqa::kTlSlots] = {};
+    return hipMemcpyToSymbol(HIP_SYMBOL(gqa::g_timeline), zeros, sizeof(zeros)) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+#else
+    return GQA_ERR_UNSUPPORTED;
+#endif
+}

@@ -32,6 +32,25 @@ extern "C" {
  */
 gqa_status gqa_hbm_stream_read(const void *buf, size_t bytes, int *sink, hipStream_t stream);
 
+/*
+ * Per-workgroup timeline of the decode kernels (diagnostic build only). The library built with
+ * GQA_TIMELINE (libgqa_timeline.so, from build.py --timeline) has thread 0 of every decode
+ * workgroup w < 4096 record the device's constant 100 MHz clock at fixed points into slots
+ * [w][0..31] of a device array (unsigned 64-bit): 0 entry; 1 sequence length(s) and work layout
+ * known; for the workgroup's piece p < 3 (a key range of one sequence and KV head), slots
+ * 2 + 6 p + 0 start, + 1 first block done, + 2 block loop done, + 3 waves merged and partials
+ * issued, + 4 arrival counted (split ranges merged in the kernel), + 5 end; 20 exit; 21 the
+ * number of pieces (a count). Slots a workgroup never reaches keep their value.
+ *
+ * gqa_timeline_clear zeroes the array; gqa_timeline_read copies its first `bytes` bytes (at
+ * most 4096 * 32 * 8) to host memory `dst`. Both are synchronous (they wait for the device's
+ * prior work) and belong between decode calls, never during one. The library proper returns
+ * GQA_ERR_UNSUPPORTED from both (and GQA_ERR_INVALID_ARG for a null dst); GQA_ERR_HIP when a
+ * copy fails.
+ */
+gqa_status gqa_timeline_read(void *dst, size_t bytes);
+gqa_status gqa_timeline_clear(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -268,3 +268,13 @@ def test_prefill_cached_rejects(lib, kw, code):
 def test_stream_read_rejects(lib, buf, nbytes, sink):
     """The streaming-read measurement call checks its arguments before any HIP call."""
     assert lib.gqa_hbm_stream_read(buf, nbytes, sink, None) == INV
+
+
+def test_timeline_calls_in_the_library_proper(lib):
+    """The per-workgroup timeline exists only in the diagnostic build: the library proper says so
+    (and refuses a null destination first), without touching the device."""
+    import ctypes
+    buf = ctypes.create_string_buffer(64)
+    assert lib.gqa_timeline_read(None, 64) == INV
+    assert lib.gqa_timeline_read(ctypes.addressof(buf), 64) == UNS
+    assert lib.gqa_timeline_clear() == UNS

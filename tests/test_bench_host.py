@@ -183,6 +183,28 @@ def test_committed_traffic_records_name_their_sources():
         assert all("gqa::" in k for k in w["kernels"]), name
 
 
+def test_timeline_summary_of_synthetic_stamps():
+    import numpy as np
+    a = np.zeros((4096, 32), dtype=np.uint64)
+    # three workgroups, clock ticks of 10 ns: entries at 0, 50, 100; one piece each (slots 2-7),
+    # the third merged last (arrival at +4); exits at 2000, 2500, 3000 ticks
+    for w in range(3):
+        base = 1000 + 50 * w
+        a[w, 0] = base
+        a[w, 1] = base + 100
+        a[w, 2:8] = [base + 100, base + 300, base + 800, base + 900, base + 950, base + 960 + 400 * (w == 2)]
+        a[w, 20] = base + 1000 + 450 * w
+        a[w, 21] = 1
+    lines = bench.timeline_summary(a, "synthetic")
+    text = "\n".join(lines)
+    assert "3 workgroups, span 20.00 us" in lines[0]   # last exit 3000 ticks, first entry 1000
+    entry = next(l for l in lines if l.strip().startswith("entry"))
+    assert entry.split()[1:] == ["0.00", "0.10", "0.50", "0.90", "1.00"]
+    loop = next(l for l in lines if "block loop done ->" in l)
+    assert loop.split()[-5:] == ["2.00", "2.90", "6.50", "10.10", "11.00"]
+    assert "workgroups with 1 piece(s):    3" in text
+
+
 # ---- one GPU only ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("argv, env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})])
