@@ -1,7 +1,8 @@
 """Benchmark of the GQA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path FAMILY]
                     [--no-cpu-baseline] [--no-breakdown]
+    python bench.py --timeline --workload NAME --steps K     (needs the timeline build)
     python bench.py --summarize-trace KERNEL_TRACE.csv --steps K
     python bench.py --summarize-counters FETCH.csv WRITE.csv --steps K --workload NAME
     python bench.py --summarize-calibration FETCH.csv WRITE.csv
@@ -29,16 +30,18 @@ The fp64 oracle is timed on the host cores beside the GPU (the headline decode, 
 prefill and the fp8 MQA decode), with the core count and CPU model.
 
 Prints one JSON line. The --summarize-* modes turn rocprofv3 output of such a run into the
-summaries kept under profiles/ (the timed dispatches only: the last K of each kernel).
+summaries kept under profiles/ (the timed dispatches only: the last K of each kernel);
+--timeline prints the per-workgroup timeline of K cold decode calls (the diagnostic build of the
+library, include/gqa_measure.h).
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import re
 import math
 import os
+import re
 import sys
 import time
 
