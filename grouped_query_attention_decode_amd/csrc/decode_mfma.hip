@@ -621,46 +621,45 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     }
 
     // ---- merge the four waves in one LDS round (fixed order: deterministic) ----
-    // Each wave rescales its accumulators to the workgroup maximum and writes them to its own
-    // slice; every thread then sums four slices for 4 consecutive head dims.
+    // Each wave writes its accumulators, reference maximum and sum to its own slice as they
+    // are; every thread then takes 4 consecutive head dims of one head and sums the four
+    // slices, each rescaled to the workgroup maximum (one barrier fewer than rescaling before
+    // the write).
     float *o_w = reinterpret_cast<float *>(lds);  // [kWaves][HP][kDP]
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         lsum[hb] = sum_xor32(sum_xor16(lsum[hb]));
-        if (lane < 16) m_w[wave][hb * 16 + lane] = m[hb];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
         const int h = hb * 16 + (lane & 15);
-        if (hb * 16 < R) {
-            float M = m_w[0][h];
+        if (h < R) {
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
-            const float f = m[hb] == -INFINITY ? 0.f : fast_exp2(m[hb] - M);
-            if (h < R) {
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb)
-                    *(f32x4_t *)&o_w[(wave * HP + h) * kDP + 16 * nb + 4 * (lane >> 4)] =
-                        f32x4_t{o[hb][nb][0] * f, o[hb][nb][1] * f, o[hb][nb][2] * f, o[hb][nb][3] * f};
-                if (lane < 16) l_w[wave][h] = lsum[hb] * f;
+            for (int nb = 0; nb < 8; ++nb)
+                *(f32x4_t *)&o_w[(wave * HP + h) * kDP + 16 * nb + 4 * (lane >> 4)] = o[hb][nb];
+            if (lane < 16) {
+                m_w[wave][h] = m[hb];
+                l_w[wave][h] = lsum[hb];
             }
         }
     }
     __syncthreads();
     for (int cidx = threadIdx.x; cidx < R * (kD / 4); cidx += kThreads) {
         const int h = cidx / (kD / 4), d = 4 * (cidx % (kD / 4));
-        f32x4_t acc = *(const f32x4_t *)&o_w[h * kDP + d];
-        float l = l_w[0][h];
+        float M = m_w[0][h];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
+        // A wave without rows of this piece holds m = -inf and zeros: weight 0.
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = m_w[w][h];
+            const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
             const f32x4_t x = *(const f32x4_t *)&o_w[(w * HP + h) * kDP + d];
-            acc[0] += x[0];
-            acc[1] += x[1];
-            acc[2] += x[2];
-            acc[3] += x[3];
-            l += l_w[w][h];
+            acc[0] += f * x[0];
+            acc[1] += f * x[1];
+            acc[2] += f * x[2];
+            acc[3] += f * x[3];
+            l += f * l_w[w][h];
         }
         if (po.direct) {
             const float inv = vscale / l;
@@ -672,12 +671,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
                 splitkv_store4c(splitkv_acc_rsrc(a, head0, R), (unsigned)(((h * S + po.slot) * kD + d) * 4), v);
             else  // read once, by the combine kernel: streamed past the caches (fp8 MQA decode -0.8 us)
                 __builtin_nontemporal_store(v, (f32x4_t *)&a.part_acc[((head0 + h) * S + po.slot) * kD + d]);
-            if (d == 0) {
-                float M = m_w[0][h];
-#pragma unroll
-                for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
-                splitkv_store_ml(&a.part_ml[((head0 + h) * S + po.slot) * 2], M, l, a.fuse_combine);
-            }
+            if (d == 0) splitkv_store_ml(&a.part_ml[((head0 + h) * S + po.slot) * 2], M, l, a.fuse_combine);
         }
     }
     tl_stamp(tls + 3);
