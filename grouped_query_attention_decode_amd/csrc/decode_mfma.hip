@@ -264,13 +264,33 @@ __device__ __forceinline__ void load_q(i32x4_t (&qT)[NHB][4], const uint16_t *qp
 // operand layout and in the V row layout alike -- put the new chunk (quantised for an fp8
 // cache) in its place and store it to the cache, so the row is written once and attended to
 // with exactly the bytes stored.
+// The current token's key and value as append_row needs them, requested when the piece starts
+// so that their round trip overlaps the block loop instead of delaying the last block: bf16,
+// the lane's 16-byte chunk of each; fp8, the four values the lane quantises and their scale.
+template <int KV> struct AppendIn;
+template <> struct AppendIn<KV_BF16> { i32x4_t k, v; };
+template <> struct AppendIn<KV_FP8> { i32x2_t w; float sc; };
+template <> struct AppendIn<KV_I4> {};
+
+template <int KV>
+__device__ __forceinline__ void load_append(AppendIn<KV> &in, const AttnArgs &a, int bg, int lane) {
+    const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (long)bg * kD;
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (long)bg * kD;
+    if constexpr (KV == KV_FP8) {
+        in.w = *(const i32x2_t *)((lane < 32 ? kn : vn) + 4 * (lane & 31));
+        in.sc = lane < 32 ? a.k_scale[bg] : a.v_scale[bg];
+    } else if constexpr (KV == KV_BF16) {
+        const int d0 = 8 * (lane & 15);
+        in.k = *(const i32x4_t *)(kn + d0);
+        in.v = *(const i32x4_t *)(vn + d0);
+    }
+}
+
 template <int KV, bool PAGED>
-__device__ __forceinline__ void append_row(Frag<KV> &f, const AttnArgs &a, int bg, const KvSrc &src, int t0, int r,
+__device__ __forceinline__ void append_row(Frag<KV> &f, const AppendIn<KV> &in, const KvSrc &src, int t0, int r,
                                            int lane) {
     constexpr int RB = kRowBytes<KV>;
     constexpr bool FP8 = KV == KV_FP8, I4 = KV == KV_I4;
-    const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (long)bg * kD;
-    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (long)bg * kD;
     const long ro = row_off<PAGED, RB>(src, fetch_pages<PAGED>(src, t0), t0, r);
     char *kr = const_cast<char *>(src.k) + ro;
     char *vr = const_cast<char *>(src.v) + ro;
@@ -279,13 +299,12 @@ __device__ __forceinline__ void append_row(Frag<KV> &f, const AttnArgs &a, int b
     // fragment stays in registers.
     if constexpr (I4) {
         // INT4 caches are appended by the copy kernel before the attention, never here.
-        (void)f; (void)kr; (void)vr; (void)rb; (void)kn; (void)vn; (void)lane;
+        (void)f; (void)in; (void)kr; (void)vr; (void)rb; (void)lane;
     } else if constexpr (FP8) {
         // The wave quantises the 256 new values once, four per lane (K dims 4l .. 4l+3 in lanes
         // 0-31, V dims in lanes 32-63), and each lane gathers the four words of its chunks.
-        const int hl = lane & 31;
-        const i32x2_t w = *(const i32x2_t *)((lane < 32 ? kn : vn) + 4 * hl);
-        const float sc = lane < 32 ? a.k_scale[bg] : a.v_scale[bg];
+        const i32x2_t w = in.w;
+        const float sc = in.sc;
         const int word = (int)quant_e4m3fn_x4(__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
                                               __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u), sc);
         auto gather = [&](int l0) { return i32x4_t{__shfl(word, l0), __shfl(word, l0 + 1), __shfl(word, l0 + 2), __shfl(word, l0 + 3)}; };
@@ -301,8 +320,8 @@ __device__ __forceinline__ void append_row(Frag<KV> &f, const AttnArgs &a, int b
             }
     } else {
         const int d0 = 8 * (lane & 15);
-        const i32x4_t xk = *(const i32x4_t *)(kn + d0);
-        const i32x4_t xv = *(const i32x4_t *)(vn + d0);
+        const i32x4_t xk = in.k;
+        const i32x4_t xv = in.v;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (4 * i + (lane >> 4) == rb) {
@@ -578,6 +597,9 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             for (int hb = 0; hb < NHB; ++hb) o[hb][nb] = mfma16x16x32(va, pb[hb], o[hb][nb]);
         }
         };
+    AppendIn<KV> ain = {};
+    if constexpr (KV != KV_I4 && NHB <= 2)  // (above 32 heads the registers are needed by the loop)
+        if (po.append) load_append<KV>(ain, a, bg, lane);
     int t0 = kb + wave * kBlockT;
     if (t0 < ke) {
         // The wave's last block is peeled off the loop: it is the one that may hold the row
@@ -587,7 +609,10 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
             step(nxt, t0, kStep, std::false_type{});
             if (t0 == kb) tl_stamp(tls + 1);
         }
-        if (po.append && tlast + kBlockT >= ke) append_row<KV, PAGED>(nxt, a, bg, src, tlast, ke - 1, lane);
+        if (po.append && tlast + kBlockT >= ke) {
+            if constexpr (KV != KV_I4 && NHB > 2) load_append<KV>(ain, a, bg, lane);
+            append_row<KV, PAGED>(nxt, ain, src, tlast, ke - 1, lane);
+        }
         step(nxt, tlast, 0, std::true_type{});
         if (tlast == kb) tl_stamp(tls + 1);
     }
@@ -791,8 +816,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
     __shared__ float m_w[kWaves][HP], l_w[kWaves][HP];
     __shared__ int lay_s[4];
-    // Clamped sequence lengths, read once by the layout step (batches of up to kLenCache
-    // sequences; larger ones read them from memory as they go).
+    // Sequence lengths as stored (clamped where used), read once by the layout step (batches of
+    // up to kLenCache sequences; larger ones read them from memory as they go).
     __shared__ int len_s[kLenCache];
 
     const int lane = threadIdx.x & 63;
@@ -809,8 +834,9 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         int Ng = 0;
         for (int k0 = 0; k0 < B; k0 += 64) {
             const int bb = k0 + lane;
-            const int t = bb < B ? clamp_len(a.seq_lens[bb], a.Tk) : 0;
-            if (cached && bb < B) len_s[bb] = t;
+            const int raw = bb < B ? a.seq_lens[bb] : 0;
+            const int t = clamp_len(raw, a.Tk);
+            if (cached && bb < B) len_s[bb] = raw;
             Ng += wave_sum(flat_span(t, a.flat_pad));
         }
         const int C = flat_chunk(G * Ng, gridDim.x, a.flat_cmin);
@@ -819,7 +845,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         if (x0 < G * Ng) {
             g0 = x0 / Ng;
             if (cached)
-                flat_find([&](int bb) { return len_s[bb]; }, B, a.flat_pad, x0 - g0 * Ng, lane, b0, p0);
+                flat_find([&](int bb) { return clamp_len(len_s[bb], a.Tk); }, B, a.flat_pad, x0 - g0 * Ng, lane, b0, p0);
             else
                 flat_find([&](int bb) { return clamp_len(a.seq_lens[bb], a.Tk); }, B, a.flat_pad, x0 - g0 * Ng, lane,
                           b0, p0);
@@ -912,7 +938,8 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
         po.slot = (int)blockIdx.x - (int)((unsigned)cur.r0 / (unsigned)C);
         po.direct = po.n_slots == 1;
         // The length as stored (not clamped) decides whether row L-1 exists for an append.
-        po.append = a.k_new && cur.ke == cur.Tb && __builtin_amdgcn_readfirstlane(a.seq_lens[cur.b]) == cur.Tb;
+        po.append = a.k_new && cur.ke == cur.Tb &&
+                    __builtin_amdgcn_readfirstlane(B <= kLenCache ? len_s[cur.b] : a.seq_lens[cur.b]) == cur.Tb;
         po.seq = npieces++;
         const float kscale = FP8 || I4 ? a.k_scale[bg] : 1.f;
         const float vscale = FP8 || I4 ? a.v_scale[bg] : 1.f;
