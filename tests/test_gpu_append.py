@@ -162,6 +162,20 @@ def test_append_out_of_range_lengths(gqa):
     check_append(gqa, c, kn, vn, ALL_RUNS)
 
 
+@pytest.mark.parametrize("B", [20, 300])
+def test_append_out_of_range_lengths_in_batches(gqa, B):
+    """The flat layout decides from the stored length whether row L-1 exists: from the lengths it
+    keeps on chip for batches of up to 256 sequences (B = 20), from memory above that (B = 300).
+    Lengths <= 0 and > T_cap sit among valid ones; only the valid ones are appended to."""
+    T_cap = 64
+    raw = [[0, -2, T_cap + 7, 1, T_cap, 33][i % 6] if i % 3 else (i * 13) % T_cap + 1 for i in range(B)]
+    c = W.make_decode(B, 8, 2, 128, [min(max(x, 0), T_cap) for x in raw], T_cap=T_cap, seed=B, name=f"append_lens_B{B}")
+    c.seq_lens = torch.tensor(raw, dtype=torch.int32)
+    poison_append_rows(c)
+    kn, vn = new_rows(c, seed=B + 1)
+    check_append(gqa, c, kn, vn, [("mfma", "flat", 0, False), ("mfma", "auto", 0, False), ("generic", "auto", 0, False)])
+
+
 def test_append_fp8_saturates(gqa):
     """New values far beyond the slab's scale saturate at +-448 * scale."""
     c = W.make_decode(2, 16, 2, 128, [100, 37], T_cap=128, kv_dtype=W.FP8, seed=8, name="append_sat")
