@@ -763,7 +763,7 @@ def main():
         return _summaries(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a design note "
+        print("bench.py measures one GPU: the library has no multi-GPU path (sharding is a design note "
               "only), so only --gpus 1 runs", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
