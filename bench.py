@@ -628,6 +628,9 @@ def timeline_summary(stamps, label):
            f"  {'last piece, durations:':44s}",
            f"  {'  block loop done -> exit':44s} {pc((exit_ - at(2))[ok])}",
            f"  {'  merge of the waves, partials issued':44s} {pc((at(3) - at(2))[ok])}",
+           f"  {'    the other waves done (barrier)':44s} {pc((us(22) - at(2))[ok])}",
+           f"  {'    partial sums written to LDS':44s} {pc((us(23) - us(22))[ok])}",
+           f"  {'    summed, partials issued':44s} {pc((at(3) - us(23))[ok])}",
            f"  {'  arrival counted (split ranges)':44s} {pc((at(4) - at(3))[ok & arrived])}",
            f"  {'  then to the end (last arriver: its merge)':44s} "
            f"{pc((at(5) - np.where(arrived, at(4), at(3)))[ok])}"]
@@ -636,6 +639,14 @@ def timeline_summary(stamps, label):
         if m.any():
             out.append(f"  workgroups with {k} piece(s): {int(m.sum()):4d}, exit median {np.median(exit_[m]):6.2f} "
                        f"max {exit_[m].max():6.2f}")
+    # Placement (slot 31): CU = (XCC, shader engine, shader array, CU) from HW_ID and XCC_ID.
+    hw = a[:, 31] & 0xFFFFFFFF
+    xcc = (a[:, 31] >> 32) & 0xF
+    cu = xcc * 1024 + ((hw >> 13) & 7) * 64 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 0xF)
+    per_cu = np.unique(cu[ok | (a[:, 0] != 0)], return_counts=True)[1]
+    hist = {int(k): int(v) for k, v in zip(*np.unique(per_cu, return_counts=True))}
+    out.append(f"  placement: {len(per_cu)} CUs used, CUs by workgroups held {hist}; XCD = blockIdx mod 8 for "
+               f"{int(((idx % 8) == xcc)[a[:, 0] != 0].sum())} of {int((a[:, 0] != 0).sum())} workgroups")
     out.append("  by blockIdx mod 8 (the XCD the dispatcher sends it to): exit median / max, last loop done median")
     for x in range(8):
         m = ((idx % 8) == x) & ok

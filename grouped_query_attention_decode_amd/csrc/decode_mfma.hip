@@ -57,9 +57,16 @@ __device__ __forceinline__ void tl_put(int slot, unsigned long long v) {
         g_timeline[blockIdx.x * kTlSlots + slot] = v;
 }
 __device__ __forceinline__ void tl_stamp(int slot) { tl_put(slot, __builtin_amdgcn_s_memrealtime()); }
+// Where the workgroup runs: the HW_ID register (CU, shader array and engine fields) in the low
+// 32 bits, XCC_ID above.
+__device__ __forceinline__ void tl_where() {
+    tl_put(31, (unsigned long long)__builtin_amdgcn_s_getreg(0xF804) |
+                   ((unsigned long long)__builtin_amdgcn_s_getreg(0xF814) << 32));
+}
 #else
 __device__ __forceinline__ void tl_put(int, unsigned long long) {}
 __device__ __forceinline__ void tl_stamp(int) {}
+__device__ __forceinline__ void tl_where() {}
 #endif
 
 namespace {
@@ -652,6 +659,7 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
     // the write).
     float *o_w = reinterpret_cast<float *>(lds);  // [kWaves][HP][kDP]
     __syncthreads();  // every wave is done with its V tile
+    tl_stamp(22);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
         lsum[hb] = sum_xor32(sum_xor16(lsum[hb]));
@@ -667,24 +675,34 @@ __device__ __forceinline__ void attend(const AttnArgs &a, char *lds, float (*m_w
         }
     }
     __syncthreads();
+    tl_stamp(23);
     for (int cidx = threadIdx.x; cidx < R * (kD / 4); cidx += kThreads) {
         const int h = cidx / (kD / 4), d = 4 * (cidx % (kD / 4));
-        float M = m_w[0][h];
+        // All twelve LDS reads of the item go out before any is used: one LDS round trip per
+        // item (left to itself, the scheduler spaces them one round trip apart).
+        float mw[kWaves], lw[kWaves];
+        f32x4_t x[kWaves];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
+        for (int w = 0; w < kWaves; ++w) {
+            mw[w] = m_w[w][h];
+            lw[w] = l_w[w][h];
+            x[w] = *(const f32x4_t *)&o_w[(w * HP + h) * kDP + d];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float M = mw[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
         // A wave without rows of this piece holds m = -inf and zeros: weight 0.
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         float l = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = m_w[w][h];
-            const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-            const f32x4_t x = *(const f32x4_t *)&o_w[(w * HP + h) * kDP + d];
-            acc[0] += f * x[0];
-            acc[1] += f * x[1];
-            acc[2] += f * x[2];
-            acc[3] += f * x[3];
-            l += f * l_w[w][h];
+            const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+            acc[0] += f * x[w][0];
+            acc[1] += f * x[w][1];
+            acc[2] += f * x[w][2];
+            acc[3] += f * x[w][3];
+            l += f * lw[w];
         }
         if (po.direct) {
             const float inv = vscale / l;
@@ -754,6 +772,7 @@ __global__ __launch_bounds__(kThreads, NHB <= 2 ? 2 : 1) void decode_mfma_kernel
     const int kb = split * a.split_len;
     const long head0 = (long)b * H + (long)g * R;  // first query head row of this group
     tl_stamp(0);
+    tl_where();
 
     // The query, the scales and this wave's first block do not depend on the length (the
     // block's rows are clamped to the allocation), so they are requested before it and share
@@ -824,6 +843,7 @@ __global__ __launch_bounds__(kThreads, NHB == 1 || (NHB == 2 && KV != KV_BF16) ?
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
     const int G = a.G, H = a.H, R = H / G, B = a.B;
     tl_stamp(0);
+    tl_where();
 
     // Layout, once per workgroup: Ng, the chunk C, and the segment holding the first row. The
     // lengths are read from memory once (into LDS, for batches up to kLenCache; the search for

@@ -40,7 +40,11 @@ gqa_status gqa_hbm_stream_read(const void *buf, size_t bytes, int *sink, hipStre
  * known; for the workgroup's piece p < 3 (a key range of one sequence and KV head), slots
  * 2 + 6 p + 0 start, + 1 first block done, + 2 block loop done, + 3 waves merged and partials
  * issued, + 4 arrival counted (split ranges merged in the kernel), + 5 end; 20 exit; 21 the
- * number of pieces (a count). Slots a workgroup never reaches keep their value.
+ * number of pieces (a count); for the workgroup's last piece, 22 all four waves' block loops done
+ * (the first barrier of the merge of the waves) and 23 the waves' partial sums written to LDS
+ * (its second barrier); 31 where the workgroup ran (a value: the HW_ID register, which holds the
+ * CU, shader-array and shader-engine numbers, in the low 32 bits, XCC_ID above). Slots a
+ * workgroup never reaches keep their value.
  *
  * gqa_timeline_clear zeroes the array; gqa_timeline_read copies its first `bytes` bytes (at
  * most 4096 * 32 * 8) to host memory `dst`. Both are synchronous (they wait for the device's

@@ -195,6 +195,13 @@ def test_timeline_summary_of_synthetic_stamps():
         a[w, 2:8] = [base + 100, base + 300, base + 800, base + 900, base + 950, base + 960 + 400 * (w == 2)]
         a[w, 20] = base + 1000 + 450 * w
         a[w, 21] = 1
+        a[w, 22] = base + 850   # waves done 0.5 us after wave 0's loop
+        a[w, 23] = base + 870   # partial sums written 0.2 us later
+    # placement: XCC 0 CU 1, XCC 1 CU 1, and the third workgroup on that same CU of XCC 1
+    # (HW_ID: CU in bits 11:8; XCC_ID above bit 32)
+    a[0, 31] = 1 << 8
+    a[1, 31] = (1 << 32) | (1 << 8)
+    a[2, 31] = (1 << 32) | (1 << 8)
     lines = bench.timeline_summary(a, "synthetic")
     text = "\n".join(lines)
     assert "3 workgroups, span 20.00 us" in lines[0]   # last exit 3000 ticks, first entry 1000
@@ -203,6 +210,13 @@ def test_timeline_summary_of_synthetic_stamps():
     loop = next(l for l in lines if "block loop done ->" in l)
     assert loop.split()[-5:] == ["2.00", "2.90", "6.50", "10.10", "11.00"]
     assert "workgroups with 1 piece(s):    3" in text
+    waves = next(l for l in lines if "the other waves done" in l)
+    assert waves.split()[-5:] == ["0.50"] * 5
+    sums = next(l for l in lines if "partial sums written" in l)
+    assert sums.split()[-5:] == ["0.20"] * 5
+    place = next(l for l in lines if "placement" in l)
+    assert "2 CUs used, CUs by workgroups held {1: 1, 2: 1}" in place
+    assert "blockIdx mod 8 for 2 of 3 workgroups" in place
 
 
 # ---- one GPU only ------------------------------------------------------------------------
